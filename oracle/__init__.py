@@ -1,0 +1,171 @@
+"""ORACLE -- test infrastructure only.
+
+A plain fp64 CPU statement of the Wan 3D-RoPE self/cross attention (see the
+header of ``wanattn_oracle.c`` for the pages and sections each function
+follows).  Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this package; the HIP library never does and
+shares no code with it.
+
+Inputs are bf16 bit patterns (uint16 numpy arrays); outputs are float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "wanattn_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# tests/test_oracle_mutants.py points this at deliberately broken builds of the
+# oracle to show that the pins catch them
+_OVERRIDE = os.environ.get("WANATTN_ORACLE_LIB")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with the host C compiler (no GPU code involved)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _OVERRIDE:
+            lib = ctypes.CDLL(_OVERRIDE)
+        else:
+            if not os.path.exists(LIB_PATH):
+                build(force=False)
+            lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        f64 = ctypes.c_double
+        lib.orc_axis_dims.argtypes = [i32, P]
+        lib.orc_axis_dims.restype = None
+        lib.orc_omega.argtypes = [f64, i32, i32]
+        lib.orc_omega.restype = f64
+        lib.orc_decode.argtypes = [i32, i32, i32, P]
+        lib.orc_decode.restype = None
+        lib.orc_rope_vec.argtypes = [P, P, i32, i32, i32, i32, f64]
+        lib.orc_rope_vec.restype = None
+        lib.orc_rope3d.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, f64]
+        lib.orc_rope3d.restype = None
+        lib.orc_self_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                      f64, f64, i32, i32, P, i32, P, P, i32]
+        lib.orc_self_rows.restype = i32
+        lib.orc_cross_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, P, i32, P, P, i32]
+        lib.orc_cross_rows.restype = i32
+        lib.orc_token_grid.argtypes = [i32, i32, i32, P]
+        lib.orc_token_grid.restype = None
+        _lib = lib
+    return _lib
+
+
+def _threads(n):
+    return int(n) if n else max(1, min(16, os.cpu_count() or 1))
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("oracle inputs are bf16 bit patterns (uint16)")
+    return a
+
+
+def axis_dims(head_dim: int):
+    out = np.zeros(3, dtype=np.int32)
+    _load().orc_axis_dims(head_dim, out.ctypes.data)
+    return tuple(int(x) for x in out)
+
+
+def omega(theta: float, D: int, k: int) -> float:
+    return float(_load().orc_omega(theta, D, k))
+
+
+def decode(n: int, H: int, W: int):
+    out = np.zeros(3, dtype=np.int32)
+    _load().orc_decode(n, H, W, out.ctypes.data)
+    return tuple(int(x) for x in out)
+
+
+def token_grid(frames: int, height: int, width: int):
+    out = np.zeros(3, dtype=np.int32)
+    _load().orc_token_grid(frames, height, width, out.ctypes.data)
+    return tuple(int(x) for x in out)
+
+
+def rope_vec(x, pos, theta: float = 10000.0):
+    """Rotate one fp64 head vector at RoPE positions pos = (pf, ph, pw)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    _load().orc_rope_vec(x.ctypes.data, y.ctypes.data, x.shape[0], int(pos[0]), int(pos[1]),
+                         int(pos[2]), theta)
+    return y
+
+
+def rope3d(x, grid, theta: float = 10000.0, offsets=(0, 0, 0)):
+    """fp64 RoPE of a bf16 tensor [B, N, heads, d] on grid (F, H, W)."""
+    x = _u16(x)
+    B, N, heads, d = x.shape
+    F, H, W = grid
+    assert N == F * H * W
+    y = np.empty(x.shape, dtype=np.float64)
+    _load().orc_rope3d(x.ctypes.data, y.ctypes.data, B, N, heads, d, F, H, W, *offsets, theta)
+    return y
+
+
+def self_rows(q, k, v, grid, rows=None, theta: float = 10000.0, scale: float | None = None,
+              block_causal: bool = False, chunk_frames: int = 1, kv_lens=None,
+              offsets=(0, 0, 0), threads: int | None = None):
+    """Self attention with 3D RoPE for query ``rows`` (all rows if None).
+
+    Returns fp64 [B, len(rows), heads, d]."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, N, heads, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    F, H, W = grid
+    if rows is None:
+        rows = np.arange(N, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    kvl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
+    out = np.empty((B, rows.shape[0], heads, d), dtype=np.float64)
+    rc = _load().orc_self_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, N, heads, d, F, H, W,
+                               int(offsets[0]), int(offsets[1]), int(offsets[2]), theta, scale,
+                               1 if block_causal else 0, int(chunk_frames),
+                               None if kvl is None else kvl.ctypes.data, rows.shape[0],
+                               rows.ctypes.data, out.ctypes.data, _threads(threads))
+    if rc != 0:
+        raise ValueError("orc_self_rows rejected its arguments")
+    return out
+
+
+def cross_rows(q, k_ctx, v_ctx, rows=None, scale: float | None = None, ctx_lens=None,
+               threads: int | None = None):
+    """Cross attention (no RoPE) for query ``rows``; fp64 [B, len(rows), heads, d]."""
+    q, k_ctx, v_ctx = _u16(q), _u16(k_ctx), _u16(v_ctx)
+    B, N, heads, d = q.shape
+    M = k_ctx.shape[1]
+    assert k_ctx.shape == (B, M, heads, d) and v_ctx.shape == k_ctx.shape
+    if rows is None:
+        rows = np.arange(N, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    cl = None if ctx_lens is None else np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    out = np.empty((B, rows.shape[0], heads, d), dtype=np.float64)
+    rc = _load().orc_cross_rows(q.ctypes.data, k_ctx.ctypes.data, v_ctx.ctypes.data, B, N, M, heads,
+                                d, scale, None if cl is None else cl.ctypes.data, rows.shape[0],
+                                rows.ctypes.data, out.ctypes.data, _threads(threads))
+    if rc != 0:
+        raise ValueError("orc_cross_rows rejected its arguments")
+    return out

@@ -1,0 +1,228 @@
+"""Benchmark of the Wan 3D-RoPE attention hot path on one MI355X.
+
+One step = one DiT-block attention pass over one batch of synthetic input:
+wanattn_self (3D RoPE fused, bidirectional or block-causal per workload)
+followed by wanattn_cross (text tokens), both through the C ABI on torch's
+current stream.  Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line (rank 0).  `value` is the step's algorithmic attention
+TFLOP/s (self + cross FLOPs / step time); the self-attention kernel's own
+rate and its fraction of the bf16 MFMA peak are in `roofline`.
+
+FLOP counts (Wan2.2 source reading (blog.leeguoo.com), ch. 8: 2 x 2 x L^2 x dim
+for the Q K^T and A V products):
+  self  = 4 * d * heads * (visible query-key pairs)   (N^2 when bidirectional)
+  cross = 4 * d * heads * N * M
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def visible_pairs(wl, kv_len=None):
+    """Query-key pairs the mask allows (block-causal: own and earlier chunks)."""
+    N = wl.N
+    L = N if kv_len is None else kv_len
+    if not wl.block_causal:
+        return N * L
+    ct = wl.chunk_frames * wl.H * wl.W
+    total = 0
+    for c0 in range(0, N, ct):
+        rows = min(ct, N - c0)
+        total += rows * min(L, c0 + ct)
+    return total
+
+
+def flops(wl):
+    d, h = wl.head_dim, wl.heads
+    return 4 * d * h * visible_pairs(wl) * wl.batch, 4 * d * h * wl.N * wl.text_len * wl.batch
+
+
+def cpu_baseline(wl, t, threads):
+    """Time the fp64 oracle on sampled query rows (all heads) and extrapolate.
+
+    t(R) = a + b R for R rows of every head (a: rotating every key of every
+    head, b: one row of every head); full self = a + b N.  Cross needs no
+    rotation: full = b_c N.  The oracle is used as it stands."""
+    import numpy as np
+    import oracle
+    from video_diffusion_transformer_wanattn_amd import seeded
+
+    grid = (wl.F, wl.H, wl.W)
+    R1, R2 = 8, 24
+    rows1 = seeded.sample_rows(wl.N, R1, seed=1)
+    rows2 = seeded.sample_rows(wl.N, R2, seed=2)
+    kw = dict(theta=10000.0, block_causal=wl.block_causal, chunk_frames=wl.chunk_frames,
+              threads=threads)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    t1 = timed(lambda: oracle.self_rows(t["q"], t["k"], t["v"], grid, rows=rows1, **kw))
+    log(f"cpu oracle: {len(rows1)} rows x {wl.heads} heads in {t1:.2f}s")
+    t2 = timed(lambda: oracle.self_rows(t["q"], t["k"], t["v"], grid, rows=rows2, **kw))
+    log(f"cpu oracle: {len(rows2)} rows x {wl.heads} heads in {t2:.2f}s")
+    b = max((t2 - t1) / (len(rows2) - len(rows1)), 1e-12)
+    a = max(t1 - b * len(rows1), 0.0)
+    if wl.block_causal:
+        # rows cost in proportion to their visible keys: scale by the mean
+        # visible fraction relative to the sampled rows' mean
+        ct = wl.chunk_frames * wl.H * wl.W
+        vis = lambda r: min(wl.N, (r // ct + 1) * ct)
+        mean_all = visible_pairs(wl) / wl.N
+        mean_s = float(np.mean([vis(r) for r in np.concatenate([rows1, rows2])]))
+        b *= mean_all / mean_s
+    rc = seeded.sample_rows(wl.N, 64, seed=3)
+    tc = timed(lambda: oracle.cross_rows(t["q"], t["text_k"], t["text_v"], rows=rc, threads=threads))
+    log(f"cpu oracle: cross {len(rc)} rows in {tc:.2f}s")
+    t_self = a + b * wl.N
+    t_cross = tc / len(rc) * wl.N
+    f_self, f_cross = flops(wl)
+    return {
+        "value": (f_self + f_cross) / (t_self + t_cross) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on {len(rows1)} and {len(rows2)} sampled query rows x {wl.heads} heads "
+                   f"(self, incl. rotating all keys) and {len(rc)} rows (cross); extrapolated as "
+                   f"t = a + b*rows to all {wl.N} rows: self {t_self:.1f} s, cross {t_cross:.1f} s "
+                   f"per step"),
+        "cpu_s_measured": t1 + t2 + tc,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b_720p_81f")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the attention kernels run on one device; "
+              "multi-GPU sharding (heads over GPUs) is described in DESIGN.md and not built",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from video_diffusion_transformer_wanattn_amd import seeded
+    from video_diffusion_transformer_wanattn_amd import wanattn as wa
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    wl = seeded.WORKLOADS[args.workload]
+    grid = (wl.F, wl.H, wl.W)
+    log(f"workload {wl.name}: grid {grid} = {wl.N} tokens x {wl.heads} heads x {wl.head_dim}, "
+        f"text {wl.text_len}, block_causal={wl.block_causal}")
+    t = seeded.workload_tensors(wl, seed=args.seed)
+    log("inputs generated")
+
+    def dev(bits):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    kc, vc = dev(t["text_k"]), dev(t["text_v"])
+    o_self = torch.empty_like(q)
+    o_cross = torch.empty_like(q)
+    wa.prepare(10000.0)
+    torch.cuda.synchronize()
+    log("inputs resident on the GPU")
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        wa.self_attention(q, k, v, grid, block_causal=wl.block_causal, chunk_frames=wl.chunk_frames,
+                          out=o_self)
+        if events is not None:
+            events[1].record(stream)
+        wa.cross_attention(q, kc, vc, out=o_cross)
+        if events is not None:
+            events[2].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup}")
+    per = [[ev(), ev(), ev()] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(per[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    self_ms = [e[0].elapsed_time(e[1]) for e in per]
+    cross_ms = [e[1].elapsed_time(e[2]) for e in per]
+    step_ms = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (self {sum(self_ms) / len(self_ms):.3f} ms, "
+        f"cross {sum(cross_ms) / len(cross_ms):.3f} ms)")
+
+    f_self, f_cross = flops(wl)
+    self_avg = sum(self_ms) / len(self_ms)
+    cross_avg = sum(cross_ms) / len(cross_ms)
+    achieved = f_self / (self_avg * 1e-3) / 1e12
+    cross_bytes = (2 * wl.N + 2 * wl.text_len) * wl.heads * wl.head_dim * 2 * wl.batch
+
+    result = {
+        "metric": "self-attn TFLOP/s + % bf16 MFMA peak at 32,760 and 75,600 tokens (1 GPU)",
+        "value": round((f_self + f_cross) / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "tokens": wl.N, "grid": list(grid),
+                   "heads": wl.heads, "head_dim": wl.head_dim, "text_tokens": wl.text_len,
+                   "mask": "block_causal" if wl.block_causal else "bidirectional",
+                   "chunk_frames": wl.chunk_frames if wl.block_causal else None,
+                   "rope_theta": 10000.0, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_fwd_kernel (wanattn_self)",
+                     "flops_per_launch": f_self},
+        "self_ms": round(self_avg, 3),
+        "self_ms_min": round(min(self_ms), 3),
+        "self_tflops": round(achieved, 2),
+        "cross_ms": round(cross_avg, 4),
+        "cross_tflops": round(f_cross / (cross_avg * 1e-3) / 1e12, 2),
+        "cross_gbs": round(cross_bytes / (cross_avg * 1e-3) / 1e9, 1),
+        "cross_frac_hbm": round(cross_bytes / (cross_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
+        result["cpu_baseline"] = cpu_baseline(wl, t, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+/*
+ * wanattn -- 3D-RoPE self attention and text cross attention of the Wan2.1/2.2
+ * video diffusion transformer, as hand-written HIP kernels for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * Pages that define the operations (titles as published):
+ *  [P1] "動画生成の勘定を明らかにする：Wan2.2 ソースコード精読" (blog.leeguoo.com)
+ *       ch. 4 "DiT: 75600 token の attention" -- full 3D joint attention over all
+ *       latent-frame tokens; subsection "3D RoPE" -- head dim 128 split 44/42/42
+ *       over time/height/width, applied to q and k as complex multiplication;
+ *       the block forward calls self_attn(x, seq_lens, grid_sizes, freqs) and
+ *       cross_attn(x, context, context_lens).
+ *       ch. 8 "75600² とは何か" -- the Q K^T and A V products, 4 L^2 dim FLOPs.
+ *  [P2] "論文解説: Wan - 大規模オープンソース動画生成モデルのアーキテクチャと訓練"
+ *       (0h-n0.github.io), section on the text encoder -- cross attention
+ *       softmax(Q K_text^T / sqrt(d_k)) V_text.
+ *  [P3] long-video survey (atlascloud.ai), "ルート3 · Self Forcing" --
+ *       bidirectional attention replaced by causal attention over chunks.
+ *
+ * Common conventions
+ *  - Tensors are caller-owned DEVICE memory on the device that owns `stream`,
+ *    bf16 bit patterns (uint16_t), contiguous [B, tokens, heads, head_dim]
+ *    with head_dim fastest, and 16-byte aligned.  head_dim must be 128.
+ *  - Tokens of an F x H x W latent grid are frame-major:
+ *    n = (f * H + h) * W + w.  RoPE positions are (f + f0, h + h0, w + w0) and
+ *    must stay below 1024 on every axis (the table length of [P1]'s
+ *    rope_params(1024, .)).
+ *  - Pair c of a head vector is (x[2c], x[2c+1]) = (real, imag); pairs 0..21
+ *    rotate with the frame position, 22..42 with the row, 43..63 with the
+ *    column; frequency k of an axis of width D is theta^(-2k/D).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work and return; success means "enqueued".  Nothing synchronises the
+ *    device, except the first use of a new theta on a device (see
+ *    wanattn_prepare).
+ *  - Errors: arguments are checked before anything is launched.
+ *    WANATTN_E_INVALID: null or misaligned pointer, sizes < 1, N != F*H*W,
+ *    positions reaching 1024, an output overlapping an input, bad lengths.
+ *    WANATTN_E_UNSUPPORTED: head_dim != 128, more batches than
+ *    WANATTN_MAX_LEN_BATCH with a length array, more distinct theta values
+ *    than the library keeps tables for.  WANATTN_E_HIP: a HIP call failed.
+ *    wanattn_last_error() gives a thread-local text for the last failure.
+ *  - Calls on different streams may run concurrently.
+ */
+#ifndef WANATTN_H
+#define WANATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WANATTN_VERSION 1
+#define WANATTN_HEAD_DIM 128
+#define WANATTN_MAX_POS 1024
+#define WANATTN_MAX_LEN_BATCH 256
+
+typedef enum wanattn_status {
+  WANATTN_OK = 0,
+  WANATTN_E_INVALID = 1,
+  WANATTN_E_UNSUPPORTED = 2,
+  WANATTN_E_HIP = 3
+} wanattn_status;
+
+/* token grid: N = F * H * W; (f0, h0, w0) are RoPE position offsets (>= 0) */
+typedef struct wanattn_grid3d {
+  int32_t F, H, W;
+  int32_t f0, h0, w0;
+} wanattn_grid3d;
+
+typedef enum wanattn_mask {
+  WANATTN_MASK_NONE = 0,         /* bidirectional, [P1] ch. 4 */
+  WANATTN_MASK_BLOCK_CAUSAL = 1  /* latent-frame chunks, [P3] Self Forcing */
+} wanattn_mask;
+
+/*
+ * [P1] ch. 4, 3D RoPE (rope_apply): y = x rotated by the 3D rotary embedding.
+ * x, y: [B, N, heads, 128] bf16; y may equal x (in place) but must not
+ * otherwise overlap it.  The rotation is done in fp32 from a table built in
+ * fp64 on the host, and rounded to bf16 (nearest even).
+ */
+wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
+                              int32_t head_dim, const wanattn_grid3d* grid, double theta,
+                              void* stream);
+
+/*
+ * [P1] ch. 4 and ch. 8: o = softmax(q' k'^T * scale + mask) v, per batch and
+ * head, where q' and k' are q and k rotated by the 3D RoPE of their tokens.
+ * q, k, v, o: [B, N, heads, 128] bf16; o must not overlap q, k or v.
+ * scale: usually 1/sqrt(128).
+ * mask: WANATTN_MASK_NONE (every query sees every key), or
+ *   WANATTN_MASK_BLOCK_CAUSAL ([P3] Self Forcing): with C = chunk_frames
+ *   latent frames per chunk counted from frame 0 of the grid, query i sees key
+ *   j iff floor(f_j / C) <= floor(f_i / C).  chunk_frames is read only in
+ *   that mode and must be >= 1.
+ * kv_lens: HOST array [B] or NULL (= N): keys j >= kv_lens[b] are excluded
+ *   ([P1] ch. 4 seq_lens; ch. 8 pads the sequence to a multiple of the
+ *   sequence-parallel size), 1 <= kv_lens[b] <= N.  Every query row is still
+ *   written.
+ * Accumulation is fp32; the MFMA operands (rotated and scaled q, rotated k,
+ * softmax probabilities, v) are bf16; o is rounded to bf16 (nearest even).
+ */
+wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o, int32_t B,
+                            int32_t N, int32_t heads, int32_t head_dim,
+                            const wanattn_grid3d* grid, double theta, float scale,
+                            wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                            void* stream);
+
+/*
+ * [P2] cross attention, called as cross_attn(x, context, context_lens) in
+ * [P1] ch. 4: o = softmax(q k_ctx^T * scale) v_ctx, no rotary embedding.
+ * q, o: [B, N, heads, 128]; k_ctx, v_ctx: [B, M, heads, 128] (M text tokens,
+ * 512 after the text projection in [P1] ch. 4).  ctx_lens: HOST array [B] or
+ * NULL (= M), 1 <= ctx_lens[b] <= M; text keys j >= ctx_lens[b] are excluded.
+ * o must not overlap the inputs.
+ */
+wanattn_status wanattn_cross(const void* q, const void* k_ctx, const void* v_ctx, void* o,
+                             int32_t B, int32_t N, int32_t M, int32_t heads, int32_t head_dim,
+                             float scale, const int32_t* ctx_lens, void* stream);
+
+/*
+ * Build and upload the rotary table for theta on the current device now
+ * (a blocking copy).  Otherwise this happens at the first call that uses
+ * theta on a device; call it before capturing such calls in a HIP graph.
+ * Up to 8 distinct theta values are kept per device.
+ */
+wanattn_status wanattn_prepare(double theta);
+
+const char* wanattn_status_string(wanattn_status s);
+const char* wanattn_last_error(void);
+int32_t wanattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WANATTN_H */

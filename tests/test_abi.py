@@ -1,0 +1,125 @@
+"""The C-ABI library loads without a GPU, exports every symbol that
+include/wanattn.h declares, and rejects bad arguments before it launches
+anything (no compute is called here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_diffusion_transformer_wanattn_amd import wanattn as wa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wanattn.h")
+
+A = ctypes.c_void_p(1 << 20)      # 16-byte aligned dummy addresses, never dereferenced
+B_ = ctypes.c_void_p(2 << 30)
+C = ctypes.c_void_p(3 << 30)
+O = ctypes.c_void_p(4 << 30)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return wa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(wanattn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declarations_are_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(wa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.wanattn_version() == 1
+    assert lib.wanattn_status_string(0) == b"ok"
+    assert lib.wanattn_status_string(1) == b"invalid argument"
+    assert lib.wanattn_status_string(2) == b"unsupported"
+    assert lib.wanattn_status_string(3) == b"HIP error"
+
+
+def g(F, H, W, f0=0, h0=0, w0=0):
+    return ctypes.byref(wa.Grid3D(F, H, W, f0, h0, w0))
+
+
+def call_self(lib, q=A, k=B_, v=C, o=O, B=1, N=24, heads=2, d=128, grid=None, theta=1e4, scale=0.088,
+              mask=0, chunk=3, lens=None):
+    grid = grid if grid is not None else g(2, 3, 4)
+    return lib.wanattn_self(q, k, v, o, B, N, heads, d, grid, theta, scale, mask, chunk, lens, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), wa.E_INVALID),
+    (dict(o=ctypes.c_void_p((4 << 30) + 8)), wa.E_INVALID),        # misaligned
+    (dict(B=0), wa.E_INVALID),
+    (dict(N=0), wa.E_INVALID),
+    (dict(heads=0), wa.E_INVALID),
+    (dict(d=64), wa.E_UNSUPPORTED),
+    (dict(N=25), wa.E_INVALID),                                   # N != F*H*W
+    (dict(grid=None, N=24), wa.E_INVALID),
+    (dict(theta=0.0), wa.E_INVALID),
+    (dict(theta=float("nan")), wa.E_INVALID),
+    (dict(scale=0.0), wa.E_INVALID),
+    (dict(mask=7), wa.E_INVALID),
+    (dict(mask=1, chunk=0), wa.E_INVALID),
+    (dict(o=A), wa.E_INVALID),                                    # o aliases q
+    (dict(o=ctypes.c_void_p((1 << 20) + 4096)), wa.E_INVALID),     # o overlaps q
+])
+def test_self_rejects(lib, kw, status):
+    if "grid" in kw and kw["grid"] is None:
+        kw = dict(kw)
+        kw["grid"] = ctypes.cast(None, ctypes.POINTER(wa.Grid3D))
+    assert call_self(lib, **kw) == status
+    assert lib.wanattn_last_error()
+
+
+def test_self_rejects_positions_beyond_table(lib):
+    assert call_self(lib, N=24, grid=g(2, 3, 4, 1023, 0, 0)) == wa.E_INVALID
+    assert call_self(lib, N=24, grid=g(2, 3, 4, 0, 1022, 0)) == wa.E_INVALID
+    assert call_self(lib, N=24, grid=g(2, 3, 4, 0, 0, -1)) == wa.E_INVALID
+
+
+def test_self_rejects_bad_lengths(lib):
+    lens = (ctypes.c_int32 * 2)(24, 25)
+    assert call_self(lib, B=2, lens=lens) == wa.E_INVALID
+    lens = (ctypes.c_int32 * 2)(0, 5)
+    assert call_self(lib, B=2, lens=lens) == wa.E_INVALID
+    big = (ctypes.c_int32 * 300)(*([24] * 300))
+    assert call_self(lib, B=300, lens=big) == wa.E_UNSUPPORTED
+
+
+def test_cross_rejects(lib):
+    def call(q=A, k=B_, v=C, o=O, B=1, N=24, M=8, heads=2, d=128, scale=0.088, lens=None):
+        return lib.wanattn_cross(q, k, v, o, B, N, M, heads, d, scale, lens, None)
+    assert call(v=None) == wa.E_INVALID
+    assert call(M=0) == wa.E_INVALID
+    assert call(d=96) == wa.E_UNSUPPORTED
+    assert call(o=B_) == wa.E_INVALID
+    assert call(lens=(ctypes.c_int32 * 1)(9)) == wa.E_INVALID
+    assert call(lens=(ctypes.c_int32 * 1)(0)) == wa.E_INVALID
+    assert call(scale=float("inf")) == wa.E_INVALID
+
+
+def test_rope3d_rejects(lib):
+    def call(x=A, y=O, B=1, N=24, heads=2, d=128, grid=None, theta=1e4):
+        return lib.wanattn_rope3d(x, y, B, N, heads, d, grid if grid is not None else g(2, 3, 4), theta, None)
+    assert call(x=None) == wa.E_INVALID
+    assert call(y=ctypes.c_void_p((1 << 20) + 16)) == wa.E_INVALID   # partial overlap
+    assert call(N=23) == wa.E_INVALID
+    assert call(d=256) == wa.E_UNSUPPORTED
+    assert call(theta=-1.0) == wa.E_INVALID
+    assert call(grid=g(2, 3, 4, 0, 0, 1021)) == wa.E_INVALID
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 24, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        wa.rope3d(x, (2, 3, 4), out=x)
+    with pytest.raises(ValueError):
+        wa.self_attention(x, x, x, (2, 3, 4), out=x)

@@ -1,0 +1,51 @@
+// Standalone 3D rotary embedding over a whole [B, N, heads, 128] bf16 tensor.
+//
+// Wan2.2 source reading (blog.leeguoo.com), ch. 4, subsection "3D RoPE": each
+// token takes the table rows of its (f, h, w) coordinates for the time, height
+// and width segments of the head (44/42/42 wide) and multiplies q or k by them
+// as complex numbers.
+//
+// Memory-bound: one thread rotates one 16-byte chunk (4 complex pairs);
+// consecutive threads cover consecutive chunks, so loads and stores are fully
+// coalesced.  Bytes moved per element: 2 read + 2 written.
+#pragma once
+
+#include "common.h"
+
+namespace wanattn {
+
+struct RopeParams {
+  const u32x4* x;
+  u32x4* y;
+  const float2* tab;
+  long long chunks;  // B * N * heads * 16
+  int N, heads, H, W;
+  int f0, h0, w0;
+  double inv_hw, inv_w;
+};
+
+__global__ void __launch_bounds__(256) rope3d_kernel(RopeParams p) {
+  long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < p.chunks; idx += stride) {
+    int dc = (int)(idx & 15);                       // 16-byte chunk in the head vector
+    long long tok_head = idx >> 4;
+    int n = (int)((tok_head / p.heads) % p.N);      // token index in its batch
+    int f, rem, h, w;
+    divmod(n, p.H * p.W, p.inv_hw, f, rem);
+    divmod(rem, p.W, p.inv_w, h, w);
+    u32x4 in = p.x[idx];
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int c = 4 * dc + e;
+      int a = pair_axis(c);
+      int pa = a == 0 ? f + p.f0 : (a == 1 ? h + p.h0 : w + p.w0);
+      float2 cs = p.tab[(a * kMaxPos + pa) * kTabStride + pair_index(c)];
+      float re = bf16_lo(in[e]), im = bf16_hi(in[e]);
+      out[e] = pack_bf16x2(re * cs.x - im * cs.y, re * cs.y + im * cs.x);
+    }
+    p.y[idx] = out;
+  }
+}
+
+}  // namespace wanattn

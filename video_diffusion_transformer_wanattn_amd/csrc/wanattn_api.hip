@@ -1,0 +1,306 @@
+// C ABI of libwanattn: argument checks, the rotary tables, kernel launches.
+// The operations are defined in include/wanattn.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "attn_fwd.h"
+#include "rope3d.h"
+#include "wanattn.h"
+
+using namespace wanattn;
+
+namespace {
+
+constexpr int kSlots = 8;       // distinct theta values kept per device
+constexpr int kMaxDevices = 64;
+
+// Rotary tables, one per theta slot, resident on every device the library runs on.
+__device__ float2 g_rope_tab[kSlots][kTabEntries];
+
+struct DeviceTables {
+  bool have_base = false;
+  float2* base = nullptr;          // device address of g_rope_tab on this device
+  double theta[kSlots];
+  int used = 0;
+};
+DeviceTables g_dev[kMaxDevices];
+std::mutex g_mu;
+
+thread_local char t_err[512] = "";
+
+wanattn_status fail(wanattn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+wanattn_status fail(wanattn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_err, sizeof t_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// Host-side table: (cos, sin) of pos * theta^(-2k/D) in fp64, stored as fp32,
+// for the time (D = 44), height (42) and width (42) segments of a 128-wide head.
+void build_table(double theta, float2* tab) {
+  const int widths[3] = {kHeadDim - 4 * (kHeadDim / 6), 2 * (kHeadDim / 6), 2 * (kHeadDim / 6)};
+  memset(tab, 0, sizeof(float2) * kTabEntries);
+  for (int a = 0; a < 3; ++a)
+    for (int k = 0; k < widths[a] / 2; ++k) {
+      const double w = std::pow(theta, -2.0 * k / widths[a]);
+      for (int pos = 0; pos < kMaxPos; ++pos) {
+        const double ang = pos * w;
+        tab[(a * kMaxPos + pos) * kTabStride + k] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+    }
+}
+
+// Device address of the table for theta on the current device (uploaded on first use).
+wanattn_status table_for(double theta, const float2** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(WANATTN_E_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(WANATTN_E_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceTables& d = g_dev[dev];
+  if (!d.have_base) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_rope_tab));
+    if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+    d.base = (float2*)ptr;
+    d.have_base = true;
+  }
+  for (int s = 0; s < d.used; ++s)
+    if (d.theta[s] == theta) {
+      *out = d.base + (size_t)s * kTabEntries;
+      return WANATTN_OK;
+    }
+  if (d.used == kSlots)
+    return fail(WANATTN_E_UNSUPPORTED, "more than %d distinct theta values on device %d", kSlots, dev);
+  static float2 host[kTabEntries];
+  build_table(theta, host);
+  float2* dst = d.base + (size_t)d.used * kTabEntries;
+  hipError_t e = hipMemcpy(dst, host, sizeof(float2) * kTabEntries, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(WANATTN_E_HIP, "table upload: %s", hipGetErrorString(e));
+  d.theta[d.used++] = theta;
+  *out = dst;
+  return WANATTN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+wanattn_status check_grid(const wanattn_grid3d* g, int32_t N) {
+  if (!g) return fail(WANATTN_E_INVALID, "grid is NULL");
+  if (g->F < 1 || g->H < 1 || g->W < 1) return fail(WANATTN_E_INVALID, "grid dims must be >= 1");
+  if ((long long)g->F * g->H * g->W != N)
+    return fail(WANATTN_E_INVALID, "N=%d != F*H*W = %d*%d*%d", N, g->F, g->H, g->W);
+  if (g->f0 < 0 || g->h0 < 0 || g->w0 < 0) return fail(WANATTN_E_INVALID, "position offsets must be >= 0");
+  if ((long long)g->F + g->f0 > kMaxPos || (long long)g->H + g->h0 > kMaxPos ||
+      (long long)g->W + g->w0 > kMaxPos)
+    return fail(WANATTN_E_INVALID, "RoPE positions must stay below %d", kMaxPos);
+  return WANATTN_OK;
+}
+
+wanattn_status check_theta(double theta) {
+  if (!(theta > 0.0) || !std::isfinite(theta)) return fail(WANATTN_E_INVALID, "theta must be finite and > 0");
+  return WANATTN_OK;
+}
+
+wanattn_status check_tensor_sizes(int32_t B, int32_t N, int32_t heads, int32_t head_dim) {
+  if (B < 1 || N < 1 || heads < 1) return fail(WANATTN_E_INVALID, "B, N and heads must be >= 1");
+  if (N > (1 << 30)) return fail(WANATTN_E_INVALID, "N=%d above 2^30 tokens", N);
+  if (head_dim != kHeadDim) return fail(WANATTN_E_UNSUPPORTED, "head_dim %d (only 128 is built)", head_dim);
+  if ((long long)B * N * heads * kHeadDim > (1ll << 40)) return fail(WANATTN_E_INVALID, "tensor too large");
+  return WANATTN_OK;
+}
+
+wanattn_status launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(WANATTN_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return WANATTN_OK;
+}
+
+#define WA_TRY(x)                        \
+  do {                                   \
+    wanattn_status st_ = (x);            \
+    if (st_ != WANATTN_OK) return st_;   \
+  } while (0)
+
+wanattn_status check_lens(int32_t B, const int32_t* lens, int32_t maxlen, const char* name) {
+  if (!lens) return WANATTN_OK;
+  if (B > WANATTN_MAX_LEN_BATCH)
+    return fail(WANATTN_E_UNSUPPORTED, "%s given for B=%d > %d", name, B, WANATTN_MAX_LEN_BATCH);
+  for (int b = 0; b < B; ++b)
+    if (lens[b] < 1 || lens[b] > maxlen)
+      return fail(WANATTN_E_INVALID, "%s[%d]=%d outside [1, %d]", name, b, lens[b], maxlen);
+  return WANATTN_OK;
+}
+
+// Launch over groups of at most WANATTN_MAX_LEN_BATCH batches so that the
+// per-batch key lengths always fit the kernel argument block.
+template <bool ROPE, bool CAUSAL>
+wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStream_t stream) {
+  const size_t qstride = (size_t)p.N * p.heads * kHeadDim, kstride = (size_t)p.Nk * p.heads * kHeadDim;
+  const uint16_t *q0 = p.q, *k0 = p.k, *v0 = p.v;
+  uint16_t* o0 = p.o;
+  p.ntq = (p.N + kBM - 1) / kBM;
+  for (int b0 = 0; b0 < B; b0 += WANATTN_MAX_LEN_BATCH) {
+    const int nb = B - b0 < WANATTN_MAX_LEN_BATCH ? B - b0 : WANATTN_MAX_LEN_BATCH;
+    p.q = q0 + (size_t)b0 * qstride;
+    p.k = k0 + (size_t)b0 * kstride;
+    p.v = v0 + (size_t)b0 * kstride;
+    p.o = o0 + (size_t)b0 * qstride;
+    for (int b = 0; b < nb; ++b) p.lens[b] = lens ? lens[b0 + b] : p.Nk;
+    p.total = nb * p.heads * p.ntq;
+    hipLaunchKernelGGL((attn_fwd_kernel<ROPE, CAUSAL>), dim3(p.total), dim3(kThreads), 0, stream, p);
+    WA_TRY(launched("attention"));
+  }
+  return WANATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wanattn_status_string(wanattn_status s) {
+  switch (s) {
+    case WANATTN_OK: return "ok";
+    case WANATTN_E_INVALID: return "invalid argument";
+    case WANATTN_E_UNSUPPORTED: return "unsupported";
+    case WANATTN_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* wanattn_last_error(void) { return t_err; }
+
+int32_t wanattn_version(void) { return WANATTN_VERSION; }
+
+wanattn_status wanattn_prepare(double theta) {
+  WA_TRY(check_theta(theta));
+  const float2* tab = nullptr;
+  return table_for(theta, &tab);
+}
+
+wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
+                              int32_t head_dim, const wanattn_grid3d* grid, double theta,
+                              void* stream) {
+  t_err[0] = 0;
+  if (!x || !y) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(y)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  WA_TRY(check_grid(grid, N));
+  WA_TRY(check_theta(theta));
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  if (x != y && overlap(x, bytes, y, bytes)) return fail(WANATTN_E_INVALID, "y partially overlaps x");
+  const float2* tab = nullptr;
+  WA_TRY(table_for(theta, &tab));
+  RopeParams p;
+  p.x = (const u32x4*)x;
+  p.y = (u32x4*)y;
+  p.tab = tab;
+  p.chunks = (long long)B * N * heads * 16;
+  p.N = N;
+  p.heads = heads;
+  p.H = grid->H;
+  p.W = grid->W;
+  p.f0 = grid->f0;
+  p.h0 = grid->h0;
+  p.w0 = grid->w0;
+  p.inv_hw = 1.0 / ((double)grid->H * grid->W);
+  p.inv_w = 1.0 / (double)grid->W;
+  long long blocks = (p.chunks + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(rope3d_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p);
+  return launched("rope3d");
+}
+
+wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o, int32_t B,
+                            int32_t N, int32_t heads, int32_t head_dim,
+                            const wanattn_grid3d* grid, double theta, float scale,
+                            wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                            void* stream) {
+  t_err[0] = 0;
+  if (!q || !k || !v || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  WA_TRY(check_grid(grid, N));
+  WA_TRY(check_theta(theta));
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
+  if (mask != WANATTN_MASK_NONE && mask != WANATTN_MASK_BLOCK_CAUSAL)
+    return fail(WANATTN_E_INVALID, "unknown mask %d", (int)mask);
+  if (mask == WANATTN_MASK_BLOCK_CAUSAL && chunk_frames < 1)
+    return fail(WANATTN_E_INVALID, "chunk_frames must be >= 1 for the block-causal mask");
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
+    return fail(WANATTN_E_INVALID, "o overlaps an input");
+  WA_TRY(check_lens(B, kv_lens, N, "kv_lens"));
+  AttnParams p;
+  memset(&p, 0, sizeof p);
+  const float2* tab = nullptr;
+  WA_TRY(table_for(theta, &tab));
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.tab = tab;
+  p.N = N;
+  p.Nk = N;
+  p.heads = heads;
+  p.qscale = scale * 1.4426950408889634f;
+  p.H = grid->H;
+  p.W = grid->W;
+  p.f0 = grid->f0;
+  p.h0 = grid->h0;
+  p.w0 = grid->w0;
+  p.inv_hw = 1.0 / ((double)grid->H * grid->W);
+  p.inv_w = 1.0 / (double)grid->W;
+  if (mask == WANATTN_MASK_BLOCK_CAUSAL) {
+    long long ct = (long long)chunk_frames * grid->H * grid->W;
+    p.chunk_tokens = (int)(ct < N ? ct : N);
+    return launch_attn<true, true>(p, B, kv_lens, (hipStream_t)stream);
+  }
+  return launch_attn<true, false>(p, B, kv_lens, (hipStream_t)stream);
+}
+
+wanattn_status wanattn_cross(const void* q, const void* k_ctx, const void* v_ctx, void* o,
+                             int32_t B, int32_t N, int32_t M, int32_t heads, int32_t head_dim,
+                             float scale, const int32_t* ctx_lens, void* stream) {
+  t_err[0] = 0;
+  if (!q || !k_ctx || !v_ctx || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k_ctx) || !aligned16(v_ctx) || !aligned16(o))
+    return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  if (M < 1) return fail(WANATTN_E_INVALID, "M must be >= 1");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
+  const size_t qbytes = (size_t)B * N * heads * kHeadDim * 2, cbytes = (size_t)B * M * heads * kHeadDim * 2;
+  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k_ctx, cbytes) || overlap(o, qbytes, v_ctx, cbytes))
+    return fail(WANATTN_E_INVALID, "o overlaps an input");
+  WA_TRY(check_lens(B, ctx_lens, M, "ctx_lens"));
+  AttnParams p;
+  memset(&p, 0, sizeof p);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k_ctx;
+  p.v = (const uint16_t*)v_ctx;
+  p.o = (uint16_t*)o;
+  p.tab = nullptr;
+  p.N = N;
+  p.Nk = M;
+  p.heads = heads;
+  p.qscale = scale * 1.4426950408889634f;
+  p.H = 1;
+  p.W = 1;
+  p.inv_hw = 1.0;
+  p.inv_w = 1.0;
+  return launch_attn<false, false>(p, B, ctx_lens, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+"""Python binding of libwanattn (ctypes).  Argument marshalling only: every
+step of the computation runs in the HIP kernels behind the C ABI declared in
+include/wanattn.h.  Tensors are torch bf16 tensors on the GPU, contiguous,
+[B, tokens, heads, 128]; work is enqueued on torch's current stream.
+
+There is no fallback: if the library is missing or the GPU is absent the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libwanattn.so")
+
+OK, E_INVALID, E_UNSUPPORTED, E_HIP = 0, 1, 2, 3
+MASK_NONE, MASK_BLOCK_CAUSAL = 0, 1
+HEAD_DIM = 128
+MAX_POS = 1024
+MAX_LEN_BATCH = 256
+
+EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_cross", "wanattn_prepare",
+           "wanattn_status_string", "wanattn_last_error", "wanattn_version")
+
+
+class WanattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"wanattn status {status}: {message}")
+        self.status = status
+
+
+class Grid3D(ctypes.Structure):
+    _fields_ = [("F", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("f0", ctypes.c_int32), ("h0", ctypes.c_int32), ("w0", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libwanattn and declare its signatures (no GPU needed for this)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing; build it with "
+                           "`python -m video_diffusion_transformer_wanattn_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, f64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_float
+    G = ctypes.POINTER(Grid3D)
+    lib.wanattn_rope3d.argtypes = [P, P, i32, i32, i32, i32, G, f64, P]
+    lib.wanattn_rope3d.restype = ctypes.c_int
+    lib.wanattn_self.argtypes = [P, P, P, P, i32, i32, i32, i32, G, f64, f32, ctypes.c_int, i32, P, P]
+    lib.wanattn_self.restype = ctypes.c_int
+    lib.wanattn_cross.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, P, P]
+    lib.wanattn_cross.restype = ctypes.c_int
+    lib.wanattn_prepare.argtypes = [f64]
+    lib.wanattn_prepare.restype = ctypes.c_int
+    lib.wanattn_status_string.argtypes = [ctypes.c_int]
+    lib.wanattn_status_string.restype = ctypes.c_char_p
+    lib.wanattn_last_error.argtypes = []
+    lib.wanattn_last_error.restype = ctypes.c_char_p
+    lib.wanattn_version.argtypes = []
+    lib.wanattn_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _raise_on(status: int):
+    if status != OK:
+        lib = load_library()
+        raise WanattnError(status, lib.wanattn_last_error().decode(errors="replace"))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _lens(lens, B):
+    if lens is None:
+        return None
+    arr = (ctypes.c_int32 * B)(*[int(x) for x in lens])
+    return arr
+
+
+def _grid(grid, offsets):
+    F, H, W = (int(x) for x in grid)
+    f0, h0, w0 = (int(x) for x in offsets)
+    return Grid3D(F, H, W, f0, h0, w0)
+
+
+def _dims(t, *others):
+    import torch
+    for x in (t, *others):
+        if x is None:
+            continue
+        if not x.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if x.dtype != torch.bfloat16:
+            raise ValueError("tensors must be bfloat16")
+        if not x.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if x.dim() != 4:
+            raise ValueError("expected [B, tokens, heads, head_dim] tensors")
+    return tuple(int(x) for x in t.shape)
+
+
+def rope3d(x, grid, theta: float = 10000.0, offsets=(0, 0, 0), out=None, stream=None):
+    """3D RoPE of x ([B, N, heads, 128] bf16); out may be x (in place)."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(x)
+    B, N, heads, d = _dims(x, out)
+    if tuple(out.shape) != tuple(x.shape):
+        raise ValueError("out must have the shape of x")
+    g = _grid(grid, offsets)
+    _raise_on(lib.wanattn_rope3d(_ptr(x), _ptr(out), B, N, heads, d, ctypes.byref(g), float(theta),
+                                 _stream(stream)))
+    return out
+
+
+def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = None,
+                   block_causal: bool = False, chunk_frames: int = 3, kv_lens=None,
+                   offsets=(0, 0, 0), out=None, stream=None):
+    """softmax(RoPE(q) RoPE(k)^T * scale) v, bidirectional or latent-frame block-causal."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    B, N, heads, d = _dims(q, k, v, out)
+    if not (tuple(k.shape) == tuple(v.shape) == tuple(out.shape) == tuple(q.shape)):
+        raise ValueError("q, k, v and out must have the same shape")
+    if kv_lens is not None and len(kv_lens) != B:
+        raise ValueError("kv_lens needs one entry per batch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    g = _grid(grid, offsets)
+    mask = MASK_BLOCK_CAUSAL if block_causal else MASK_NONE
+    lens = _lens(kv_lens, B)
+    _raise_on(lib.wanattn_self(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, heads, d, ctypes.byref(g),
+                               float(theta), float(scale), mask, int(chunk_frames), lens,
+                               _stream(stream)))
+    return out
+
+
+def cross_attention(q, k_ctx, v_ctx, scale: float | None = None, ctx_lens=None, out=None,
+                    stream=None):
+    """softmax(q k_ctx^T * scale) v_ctx over M text tokens, no RoPE."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    B, N, heads, d = _dims(q, k_ctx, v_ctx, out)
+    M = int(k_ctx.shape[1])
+    if tuple(k_ctx.shape) != (B, M, heads, d) or tuple(v_ctx.shape) != (B, M, heads, d):
+        raise ValueError("k_ctx and v_ctx must be [B, M, heads, head_dim] like q")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    if ctx_lens is not None and len(ctx_lens) != B:
+        raise ValueError("ctx_lens needs one entry per batch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = _lens(ctx_lens, B)
+    _raise_on(lib.wanattn_cross(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(out), B, N, M, heads, d,
+                                float(scale), lens, _stream(stream)))
+    return out
+
+
+def prepare(theta: float = 10000.0):
+    _raise_on(load_library().wanattn_prepare(float(theta)))

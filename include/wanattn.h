@@ -98,6 +98,12 @@ wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int3
  *   ([P1] ch. 4 seq_lens; ch. 8 pads the sequence to a multiple of the
  *   sequence-parallel size), 1 <= kv_lens[b] <= N.  Every query row is still
  *   written.
+ * workspace: caller-owned device memory of at least
+ *   wanattn_self_workspace_bytes(B, N, heads, head_dim) bytes, 16-byte
+ *   aligned, not overlapping q, k, v or o.  It receives the rotated keys k'
+ *   (one rotation per key, shared by every query tile); its contents after the
+ *   call are unspecified.  Calls that may run concurrently need separate
+ *   workspaces.
  * Accumulation is fp32; the MFMA operands (rotated and scaled q, rotated k,
  * softmax probabilities, v) are bf16; o is rounded to bf16 (nearest even).
  */
@@ -105,7 +111,10 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
                             int32_t N, int32_t heads, int32_t head_dim,
                             const wanattn_grid3d* grid, double theta, float scale,
                             wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
-                            void* stream);
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* bytes of workspace wanattn_self needs for these sizes (0 for invalid sizes) */
+size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim);
 
 /*
  * [P2] cross attention, called as cross_attn(x, context, context_lens) in

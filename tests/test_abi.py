@@ -16,6 +16,7 @@ A = ctypes.c_void_p(1 << 20)      # 16-byte aligned dummy addresses, never deref
 B_ = ctypes.c_void_p(2 << 30)
 C = ctypes.c_void_p(3 << 30)
 O = ctypes.c_void_p(4 << 30)
+WS = ctypes.c_void_p(5 << 30)
 
 
 @pytest.fixture(scope="module")
@@ -48,9 +49,10 @@ def g(F, H, W, f0=0, h0=0, w0=0):
 
 
 def call_self(lib, q=A, k=B_, v=C, o=O, B=1, N=24, heads=2, d=128, grid=None, theta=1e4, scale=0.088,
-              mask=0, chunk=3, lens=None):
+              mask=0, chunk=3, lens=None, ws=WS, ws_bytes=1 << 20):
     grid = grid if grid is not None else g(2, 3, 4)
-    return lib.wanattn_self(q, k, v, o, B, N, heads, d, grid, theta, scale, mask, chunk, lens, None)
+    return lib.wanattn_self(q, k, v, o, B, N, heads, d, grid, theta, scale, mask, chunk, lens, ws,
+                            ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -69,6 +71,10 @@ def call_self(lib, q=A, k=B_, v=C, o=O, B=1, N=24, heads=2, d=128, grid=None, th
     (dict(mask=1, chunk=0), wa.E_INVALID),
     (dict(o=A), wa.E_INVALID),                                    # o aliases q
     (dict(o=ctypes.c_void_p((1 << 20) + 4096)), wa.E_INVALID),     # o overlaps q
+    (dict(ws=None), wa.E_INVALID),
+    (dict(ws=ctypes.c_void_p((5 << 30) + 4)), wa.E_INVALID),      # misaligned workspace
+    (dict(ws_bytes=24 * 2 * 128 * 2 - 16), wa.E_INVALID),          # workspace too small
+    (dict(ws=ctypes.c_void_p((2 << 30) + 256)), wa.E_INVALID),     # workspace overlaps k
 ])
 def test_self_rejects(lib, kw, status):
     if "grid" in kw and kw["grid"] is None:
@@ -76,6 +82,12 @@ def test_self_rejects(lib, kw, status):
         kw["grid"] = ctypes.cast(None, ctypes.POINTER(wa.Grid3D))
     assert call_self(lib, **kw) == status
     assert lib.wanattn_last_error()
+
+
+def test_workspace_size(lib):
+    assert lib.wanattn_self_workspace_bytes(2, 24, 3, 128) == 2 * 24 * 3 * 128 * 2
+    assert lib.wanattn_self_workspace_bytes(2, 24, 3, 64) == 0
+    assert lib.wanattn_self_workspace_bytes(0, 24, 3, 128) == 0
 
 
 def test_self_rejects_positions_beyond_table(lib):
@@ -90,7 +102,7 @@ def test_self_rejects_bad_lengths(lib):
     lens = (ctypes.c_int32 * 2)(0, 5)
     assert call_self(lib, B=2, lens=lens) == wa.E_INVALID
     big = (ctypes.c_int32 * 300)(*([24] * 300))
-    assert call_self(lib, B=300, lens=big) == wa.E_UNSUPPORTED
+    assert call_self(lib, B=300, lens=big, ws_bytes=1 << 28) == wa.E_UNSUPPORTED
 
 
 def test_cross_rejects(lib):

@@ -2,39 +2,46 @@
 //
 // What it computes (per batch b, head, query row i):
 //   o_i = sum_j p_ij v_j,  p_ij = softmax_j(q'_i . k'_j * scale) over visible j
-// where q', k' are q, k rotated by the 3D RoPE of their tokens (self attention,
-// Wan2.2 source reading (blog.leeguoo.com) ch. 4, "3D RoPE") or left as they
-// are (cross attention to text tokens, Wan paper explainer (0h-n0.github.io),
-// text-encoder section).  The N x N score matrix is never stored (ch. 8 of the
-// source reading sizes it; the long-video survey (atlascloud.ai) puts it at
-// ~10 GB for 32.7k tokens): scores are produced tile by tile and folded into a
-// running softmax.
+// where q' is q rotated by the 3D RoPE of its token (self attention, Wan2.2
+// source reading (blog.leeguoo.com) ch. 4, "3D RoPE") or left as it is (cross
+// attention to text tokens, Wan paper explainer (0h-n0.github.io), text-encoder
+// section), and k' is the key as the caller hands it in: for self attention the
+// library first rotates k once into a workspace with the rope3d kernel.  The
+// N x N score matrix is never stored (ch. 8 of the source reading sizes it; the
+// long-video survey (atlascloud.ai) puts it at ~10 GB for 32.7k tokens).
 //
 // Work decomposition
 //   one workgroup = 4 waves = 256 query rows of one (batch, head); a wave owns
-//   64 rows as two 32-row MFMA blocks.  Keys stream through LDS in tiles of 64,
-//   double buffered, one barrier per tile.
+//   64 rows as two 32-row MFMA blocks.  Keys stream through LDS in tiles of 64
+//   (K' 16 KiB + V 16 KiB), 4 stages, filled with global_load_lds_dwordx4 (no
+//   staging registers), two tiles in flight ahead of the one being computed.
 //
-// Per 64-key tile and wave:
-//   S^T (keys x queries) = K' Q'^T   v_mfma_f32_32x32x16_bf16, 2 x 2 x 8 issues
-//   online softmax on S^T: a lane holds 32 scores of ONE query, so row max and
-//   row sum are in-lane plus one permlane32 swap
-//   O^T (d x queries) += V^T P^T     2 x 4 x 4 issues; P stays in registers
+// Per 32-key block and wave (two blocks per tile):
+//   S^T (keys x queries) = K' Q'^T   v_mfma_f32_32x32x16_bf16, 2 x 8 issues
+//   online softmax on S^T: a lane holds 16 scores of ONE query per block, so
+//   row max and row sum are in-lane plus one permlane32 swap
+//   O^T (d x queries) += V^T P^T     2 x 4 x 2 issues; P stays in registers
+// The loop is software-pipelined over blocks: the QK^T products of block j+1
+// are issued next to the exp/convert work of block j, and the PV products of
+// block j next to the row max of block j+1.
 //
 // Key order inside a 32-key MFMA block is free (the contraction is a sum), so
-// the K rows are stored in LDS permuted (bits 2 and 3 of the key index swapped):
-// the S^T accumulator of lane l (half hh = l / 32) then holds, at register
-// positions 8s .. 8s+7, the physical keys 16s + 8hh + 0..7 -- exactly the B
-// operand layout of the PV product, so P never leaves registers.  V is kept
-// row-major in LDS and read with ds_read_b64_tr_b16, which hands each lane
-// four keys of one d column.
+// K rows sit in LDS permuted (bits 2 and 3 of the key index swapped): the S^T
+// accumulator of lane l (half hh = l / 32) then holds, at register positions
+// 8s .. 8s+7, the physical keys 16s + 8hh + 0..7 -- exactly the B operand
+// layout of the PV product.  V stays row-major in LDS and is read with
+// ds_read_b64_tr_b16, which hands each lane four keys of one d column.  Both
+// tiles XOR-swizzle their 16-byte chunks so that the MFMA operand reads are
+// free of bank conflicts.
 //
-// Softmax is in base 2: the query is multiplied by scale * log2(e) while it is
-// rotated, so p = exp2(s - m) maps to v_exp_f32.  The running max is only moved
-// when a row's tile max exceeds it by more than 8 (p <= 256 in between), which
+// Softmax is in base 2: the query is multiplied by scale * log2(e) when it is
+// loaded, so p = exp2(s - m) maps to v_exp_f32.  The running max is only moved
+// when a row's block max exceeds it by more than 8 (p <= 256 in between), which
 // makes the O rescale rare; the result is the same softmax (the final division
 // by the running sum uses the same reference point).
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 #include "wanattn.h"
@@ -45,20 +52,20 @@ constexpr int kBM = 256;                       // query rows per workgroup
 constexpr int kBN = 64;                        // keys per LDS tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKRow = 272;                     // bytes per K row in LDS (256 + 16 pad)
-constexpr int kKTile = kBN * kKRow;            // 17408
-constexpr int kVRow = 256;                     // V rows unpadded; 16-byte chunks XOR-swizzled
-constexpr int kVTile = kBN * kVRow;            // 16384
-constexpr int kStage = kKTile + kVTile;        // 33792
-constexpr int kLdsBytes = 2 * kStage;          // 67584 (of 160 KiB)
+constexpr int kRowBytes = 256;                 // one 128-wide bf16 row
+constexpr int kHalfTile = kBN * kRowBytes;     // 16 KiB: K' or V of one tile
+constexpr int kTileBytes = 2 * kHalfTile;      // 32 KiB
+constexpr int kStages = 4;
+constexpr int kLdsBytes = kStages * kTileBytes;  // 128 KiB of 160
+constexpr int kLoadsPerTile = 8;               // global_load_lds per thread per tile (4 K + 4 V)
 constexpr float kLazyRescale = 8.0f;           // log2 units
 
 struct AttnParams {
   const uint16_t* q;
-  const uint16_t* k;
+  const uint16_t* k;  // keys as used in the product (already rotated for self attention)
   const uint16_t* v;
   uint16_t* o;
-  const float2* tab;  // rotary table (self attention only)
+  const float2* tab;  // rotary table for the query (self attention only)
   int N;              // query tokens per batch
   int Nk;             // key tokens per batch
   int heads;
@@ -71,14 +78,13 @@ struct AttnParams {
   int lens[WANATTN_MAX_LEN_BATCH];  // visible keys per batch (1..Nk)
 };
 
-// K row slot of physical key t inside a 64-key tile: swap bits 2 and 3
-__device__ __forceinline__ int k_slot(int t) {
-  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
-}
-// byte offset of 16-byte chunk c of V row t inside a V tile
-__device__ __forceinline__ int v_off(int t, int c) { return t * kVRow + 16 * (c ^ (4 * (t & 3))); }
+// K row slot of physical key t inside a tile: swap bits 2 and 3 (an involution)
+__device__ __forceinline__ int k_slot(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+// 16-byte chunk swizzles (chunk index 0..15 within a 256-byte row)
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return 4 * (row & 3); }
 
-template <bool ROPE, bool CAUSAL>
+template <bool CAUSAL>
 __device__ __forceinline__ int row_limit(const AttnParams& p, int kvl, int i) {
   int lim = kvl;
   if (CAUSAL) {
@@ -104,9 +110,36 @@ __device__ __forceinline__ uint32_t rotate_pair(uint32_t w, const float2* tab, i
   return pack_bf16x2(re * scale, im * scale);
 }
 
+// wait until at most n of this wave's vector-memory operations are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  if constexpr (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (n == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else static_assert(n == 0 || n == 8, "unsupported count");
+}
+
+// workgroup barrier without the memory fence of __syncthreads (which would
+// drain the prefetches in flight); LDS reads of this wave are completed first
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <bool ROPE, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  // one LDS object per stage: accesses to different stages then carry distinct
+  // alias scopes, so the compiler's wait for a stage's direct-to-LDS loads does
+  // not also wait for the loads still filling the other stages
+  __shared__ __attribute__((aligned(1024))) char st0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char st1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char st2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char st3[kTileBytes];
+  auto stage = [&](auto S) __attribute__((always_inline)) -> char* {
+    constexpr int s_ = decltype(S)::value;
+    if constexpr (s_ == 0) return st0;
+    else if constexpr (s_ == 1) return st1;
+    else if constexpr (s_ == 2) return st2;
+    else return st3;
+  };
 
   // ---- workgroup -> (batch, head, query tile).  Workgroup w runs on XCD w % 8;
   // give each XCD a contiguous run of tiles so that the concurrent workgroups of
@@ -120,18 +153,50 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   const int b = bh / p.heads, head = bh - b * p.heads;
   const int i0 = tq * kBM;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, hh = lane >> 5;
   const int kvl = p.lens[b];
   const int i_last = min(i0 + kBM, p.N) - 1;
-  const int kv_end = row_limit<ROPE, CAUSAL>(p, kvl, i_last);
-  const int kv_full = row_limit<ROPE, CAUSAL>(p, kvl, i0);
+  const int kv_end = row_limit<CAUSAL>(p, kvl, i_last);
+  const int kv_full = row_limit<CAUSAL>(p, kvl, i0);
   const int nt = (kv_end + kBN - 1) / kBN;
+  const int nb = 2 * nt;
 
   const size_t row_stride = (size_t)p.heads * kHeadDim;  // elements between tokens
   const uint16_t* qbase = p.q + ((size_t)b * p.N * p.heads + head) * kHeadDim;
   const uint16_t* kbase = p.k + ((size_t)b * p.Nk * p.heads + head) * kHeadDim;
   const uint16_t* vbase = p.v + ((size_t)b * p.Nk * p.heads + head) * kHeadDim;
+
+  // ---- tile loads straight into LDS.  Instruction i of wave w fills 1 KiB =
+  // rows 4(4w+i) .. +3 of the K' and V halves; lane l supplies row
+  // 4(4w+i) + l/16, stored chunk l%16, i.e. global chunk (l%16) ^ swizzle(row).
+  const int ld_row = lane >> 4, ld_chunk = lane & 15;
+  auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {
+    char* st = stage(S);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = 4 * wave + i;
+      const int m = 4 * blk + ld_row;
+      const int kkey = min(t * kBN + k_slot(m), p.Nk - 1);
+      const int vkey = min(t * kBN + m, p.Nk - 1);
+      const uint16_t* ks = kbase + (size_t)kkey * row_stride + 8 * (ld_chunk ^ k_swz(m));
+      const uint16_t* vs = vbase + (size_t)vkey * row_stride + 8 * (ld_chunk ^ v_swz(m));
+      __builtin_amdgcn_global_load_lds((const void*)ks,
+                                       (__attribute__((address_space(3))) void*)(st + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)vs, (__attribute__((address_space(3))) void*)(st + kHalfTile + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+
+  // prefetch the first two tiles while the queries are loaded
+  issue_tile(S0{}, 0);
+  if (nt > 1) issue_tile(S1{}, 1);
 
   // ---- Q: load, rotate, scale, round to bf16; kept in registers as the B
   // operand of K Q^T: lane holds d = 16 kk + 8 hh + 0..7 of its query.
@@ -142,7 +207,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     const int i = i0 + wave * 64 + qb * 32 + r;
     const bool valid = i < p.N;
     const int ic = valid ? i : p.N - 1;
-    lim[qb] = row_limit<ROPE, CAUSAL>(p, kvl, ic);
+    lim[qb] = row_limit<CAUSAL>(p, kvl, ic);
     int pf = 0, ph = 0, pw = 0;
     if (ROPE) {
       int f, rm, h, w;
@@ -155,7 +220,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     const u32x4* src = (const u32x4*)(qbase + (size_t)ic * row_stride);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      u32x4 raw = valid ? src[2 * kk + hh] : u32x4{0, 0, 0, 0};
+      u32x4 raw = src[2 * kk + hh];
       u32x4 pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -163,41 +228,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       qf[qb][kk] = __builtin_bit_cast(bf16x8, pk);
     }
   }
-
-  // ---- K/V staging through registers: thread (g, dc) moves chunk dc of keys
-  // 4g .. 4g+3 of a tile; 16 consecutive threads read one 256-byte row.
-  const int dc = tid & 15, g = tid >> 4;
-  u32x4 kr[4], vr[4];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int key = t * kBN + 4 * g + rr;
-      const bool valid = key < p.Nk;
-      const size_t off = (size_t)(valid ? key : 0) * row_stride + 8 * dc;
-      kr[rr] = valid ? *(const u32x4*)(kbase + off) : u32x4{0, 0, 0, 0};
-      vr[rr] = valid ? *(const u32x4*)(vbase + off) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int t, int buf) {
-    char* kt = smem + buf * kStage;
-    char* vt = kt + kKTile;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int tk = 4 * g + rr;
-      u32x4 kv = kr[rr];
-      if (ROPE) {
-        const int key = min(t * kBN + tk, p.Nk - 1);
-        int f, rm, h, w;
-        divmod(key, p.H * p.W, p.inv_hw, f, rm);
-        divmod(rm, p.W, p.inv_w, h, w);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          kv[e] = rotate_pair<true>(kv[e], p.tab, 4 * dc + e, f + p.f0, h + p.h0, w + p.w0, 1.0f);
-      }
-      *(u32x4*)(kt + k_slot(tk) * kKRow + 16 * dc) = kv;
-      *(u32x4*)(vt + v_off(tk, dc)) = vr[rr];
-    }
-  };
 
   floatx16 acc[2][4];
 #pragma unroll
@@ -208,62 +238,53 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       for (int j = 0; j < 16; ++j) acc[qb][db][j] = 0.0f;
   float mrun[2] = {-1e30f, -1e30f}, lrun[2] = {0.0f, 0.0f};
 
-  // per-lane pieces of the V transpose-read address (see the header comment)
-  const int vg = lane >> 4;            // 16-lane group: hh = vg >> 1, d half = vg & 1
-  const int vu = (lane & 15) >> 2;     // key offset supplied by this lane
-  const int vq = lane & 3;             // d quad supplied by this lane
+  // per-lane pieces of the V transpose-read address
+  const int vg = lane >> 4;         // 16-lane group: hh = vg >> 1, d half = vg & 1
+  const int vu = (lane & 15) >> 2;  // key offset supplied by this lane
+  const int vq = lane & 3;          // d quad supplied by this lane
 
-  load_tile(0);
-  store_tile(0, 0);
-  __syncthreads();
-
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) load_tile(t + 1);
-    const char* kt = smem + buf * kStage;
-    const char* vt = kt + kKTile;
-
-    // S^T = K' Q'^T
-    floatx16 s[2][2];
+  // S^T of half kb (32 keys) of the tile in stage S into s
+  auto qk_block = [&](auto S, int kb, floatx16 (&s)[2]) {
+    const char* kt = stage(S) + kb * 32 * kRowBytes;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        s[0][kb][j] = 0.0f;
-        s[1][kb][j] = 0.0f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        bf16x8 a = *(const bf16x8*)(kt + (32 * kb + r) * kKRow + 32 * kk + 16 * hh);
-        s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][kk], s[0][kb], 0, 0, 0);
-        s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][kk], s[1][kb], 0, 0, 0);
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 a = *(const bf16x8*)(kt + r * kRowBytes + 16 * ((2 * kk + hh) ^ (r & 15)));
+      if (kk == 0) {
+        const floatx16 z = {};
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][0], z, 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][0], z, 0, 0, 0);
+      } else {
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][kk], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][kk], s[1], 0, 0, 0);
       }
     }
-
-    // visibility: key index of register j of block kb is 32 kb + 16 (j/8) + 8 hh + j%8
-    if (t * kBN + kBN > kv_full) {
+  };
+  // visibility of block j: key of register e is 32 j + 16 (e/8) + 8 hh + e%8
+  auto mask_block = [&](int j, floatx16 (&s)[2]) {
+    if (32 * j + 32 > kv_full) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = t * kBN + 32 * kb + 16 * (j >> 3) + 8 * hh + (j & 7);
-            if (key >= lim[qb]) s[qb][kb][j] = -__builtin_inff();
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int key = 32 * j + 16 * (e >> 3) + 8 * hh + (e & 7);
+          if (key >= lim[qb]) s[qb][e] = -__builtin_inff();
+        }
     }
-
-    // online softmax (base 2) and P = exp2(S - m) packed as bf16 MFMA operands
-    bf16x8 pb[2][2][2];
+  };
+  auto block_max = [&](floatx16 (&s)[2], float (&mx)[2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = -__builtin_inff();
+      float m0 = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(s[qb][e], s[qb][e + 1]));
+      mx[qb] = wave_half_max(m0);
+    }
+  };
+  // move the running max when it is exceeded by more than kLazyRescale
+  auto update_max = [&](float (&mx)[2]) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[qb][kb][j]);
-      mx = wave_half_max(mx);
-      const float mnew = fmaxf(mrun[qb], mx);
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mnew = fmaxf(mrun[qb], mx[qb]);
       const bool need = mnew > mrun[qb] + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(need)) {
         const float alpha = need ? __builtin_amdgcn_exp2f(mrun[qb] - mnew) : 1.0f;
@@ -272,57 +293,103 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) acc[qb][db][j] *= alpha;
+          for (int e = 0; e < 16; ++e) acc[qb][db][e] *= alpha;
       }
-      float sum = 0.0f;
+    }
+  };
+  // P = exp2(S - m) as bf16 MFMA operands, row sums into lrun
+  auto exp_block = [&](floatx16 (&s)[2], bf16x8 (&pb)[2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       const float m = mrun[qb];
+      float sum = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int sl = 0; sl < 2; ++sl) {
+        u32x4 pk;
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(s[qb][kb][8 * sl + 2 * e] - m);
-            const float p1 = __builtin_amdgcn_exp2f(s[qb][kb][8 * sl + 2 * e + 1] - m);
-            sum += p0 + p1;
-            pk[e] = pack_bf16x2(p0, p1);
-          }
-          pb[qb][kb][sl] = __builtin_bit_cast(bf16x8, pk);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(s[qb][8 * sl + 2 * e] - m);
+          const float p1 = __builtin_amdgcn_exp2f(s[qb][8 * sl + 2 * e + 1] - m);
+          sum += p0 + p1;
+          pk[e] = pack_bf16x2(p0, p1);
         }
+        pb[qb][sl] = __builtin_bit_cast(bf16x8, pk);
       }
       lrun[qb] += sum;
     }
-
-    // O^T += V^T P^T; V read transposed from its row-major LDS tile
+  };
+  // O^T += V^T P^T for half kb of the tile in stage S
+  auto pv_block = [&](auto S, int kb, const bf16x8 (&pb)[2][2]) {
+    const char* vt = stage(S) + kHalfTile;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int sl = 0; sl < 2; ++sl) {
+        shortx4 tr[2];
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          shortx4 tr[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int key = 32 * kb + 16 * sl + 8 * (vg >> 1) + 4 * e + vu;
-            const int chunk = 4 * db + 2 * (vg & 1) + (vq >> 1);
-            const char* addr = vt + v_off(key, chunk) + 8 * (vq & 1);
-            tr[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) shortx4*)(addr));
-          }
-          // whole-vector casts: element-wise assembly of this operand was
-          // lowered to a splat of element 0 by the compiler
-          const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, tr[0]),
-                                                   __builtin_bit_cast(bf16x4, tr[1]), 0, 1, 2, 3, 4,
-                                                   5, 6, 7);
-          acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][kb][sl], acc[0][db], 0, 0, 0);
-          acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][kb][sl], acc[1][db], 0, 0, 0);
+        for (int e = 0; e < 2; ++e) {
+          const int key = 32 * kb + 16 * sl + 8 * (vg >> 1) + 4 * e + vu;
+          const int chunk = 4 * db + 2 * (vg & 1) + (vq >> 1);
+          const char* addr = vt + key * kRowBytes + 16 * (chunk ^ v_swz(key)) + 8 * (vq & 1);
+          tr[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(addr));
         }
+        // whole-vector casts: assembling this operand element by element was
+        // lowered to a splat of element 0 by the compiler
+        const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, tr[0]),
+                                                 __builtin_bit_cast(bf16x4, tr[1]), 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][sl], acc[0][db], 0, 0, 0);
+        acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][sl], acc[1][db], 0, 0, 0);
       }
     }
+  };
 
-    if (t + 1 < nt) store_tile(t + 1, buf ^ 1);
-    __syncthreads();
+  // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored
+  if (nt > 1) wait_vm<8>();
+  else wait_vm<0>();
+  tile_barrier();
+  if (nt > 2) issue_tile(S2{}, 2);
+
+  floatx16 s_next[2];
+  float mx[2];
+  qk_block(S0{}, 0, s_next);
+  mask_block(0, s_next);
+  block_max(s_next, mx);
+  update_max(mx);
+
+  // one pipelined step: finish block j (scored in s_next), score block j+1
+  auto block_step = [&](auto S, auto SN, int j, int kb, bool has_next) __attribute__((always_inline)) {
+    floatx16 s_cur[2] = {s_next[0], s_next[1]};
+    bf16x8 pb[2][2];
+    if (has_next) {
+      if (kb == 0) qk_block(S, 1, s_next);
+      else qk_block(SN, 0, s_next);
+    }
+    exp_block(s_cur, pb);
+    pv_block(S, kb, pb);
+    if (has_next) {
+      mask_block(j + 1, s_next);
+      block_max(s_next, mx);
+      update_max(mx);
+    }
+  };
+  // tile t in stage S: its two blocks; before scoring the first block of tile
+  // t+1 (stage SN) make that tile resident and request tile t+2 into stage SNN
+  auto tile_step = [&](auto S, auto SN, auto SNN, int t) __attribute__((always_inline)) {
+    block_step(S, SN, 2 * t, 0, true);
+    const bool next_tile = t + 1 < nt;
+    if (next_tile) {
+      if (t + 2 < nt) wait_vm<8>();
+      else wait_vm<0>();
+      tile_barrier();
+      if (t + 3 < nt) issue_tile(SNN, t + 3);
+    }
+    block_step(S, SN, 2 * t + 1, 1, next_tile);
+  };
+  for (int t = 0; t < nt; t += 4) {
+    tile_step(S0{}, S1{}, S3{}, t);
+    if (t + 1 < nt) tile_step(S1{}, S2{}, S0{}, t + 1);
+    if (t + 2 < nt) tile_step(S2{}, S3{}, S1{}, t + 2);
+    if (t + 3 < nt) tile_step(S3{}, S0{}, S2{}, t + 3);
   }
 
   // ---- epilogue: O = O^T / l, bf16; lane holds d = 32 db + 8 g4 + 4 hh + 0..3

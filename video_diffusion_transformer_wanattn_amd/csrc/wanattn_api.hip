@@ -165,6 +165,40 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
   return WANATTN_OK;
 }
 
+// 3D RoPE of a whole tensor on `stream` (checked arguments)
+wanattn_status rope3d_checked(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
+                              int32_t head_dim, const wanattn_grid3d* grid, double theta,
+                              hipStream_t stream) {
+  t_err[0] = 0;
+  if (!x || !y) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(y)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  WA_TRY(check_grid(grid, N));
+  WA_TRY(check_theta(theta));
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  if (x != y && overlap(x, bytes, y, bytes)) return fail(WANATTN_E_INVALID, "y partially overlaps x");
+  const float2* tab = nullptr;
+  WA_TRY(table_for(theta, &tab));
+  RopeParams p;
+  p.x = (const u32x4*)x;
+  p.y = (u32x4*)y;
+  p.tab = tab;
+  p.chunks = (long long)B * N * heads * 16;
+  p.N = N;
+  p.heads = heads;
+  p.H = grid->H;
+  p.W = grid->W;
+  p.f0 = grid->f0;
+  p.h0 = grid->h0;
+  p.w0 = grid->w0;
+  p.inv_hw = 1.0 / ((double)grid->H * grid->W);
+  p.inv_w = 1.0 / (double)grid->W;
+  long long blocks = (p.chunks + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(rope3d_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return launched("rope3d");
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,41 +226,19 @@ wanattn_status wanattn_prepare(double theta) {
 wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
                               int32_t head_dim, const wanattn_grid3d* grid, double theta,
                               void* stream) {
-  t_err[0] = 0;
-  if (!x || !y) return fail(WANATTN_E_INVALID, "null tensor pointer");
-  if (!aligned16(x) || !aligned16(y)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
-  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
-  WA_TRY(check_grid(grid, N));
-  WA_TRY(check_theta(theta));
-  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
-  if (x != y && overlap(x, bytes, y, bytes)) return fail(WANATTN_E_INVALID, "y partially overlaps x");
-  const float2* tab = nullptr;
-  WA_TRY(table_for(theta, &tab));
-  RopeParams p;
-  p.x = (const u32x4*)x;
-  p.y = (u32x4*)y;
-  p.tab = tab;
-  p.chunks = (long long)B * N * heads * 16;
-  p.N = N;
-  p.heads = heads;
-  p.H = grid->H;
-  p.W = grid->W;
-  p.f0 = grid->f0;
-  p.h0 = grid->h0;
-  p.w0 = grid->w0;
-  p.inv_hw = 1.0 / ((double)grid->H * grid->W);
-  p.inv_w = 1.0 / (double)grid->W;
-  long long blocks = (p.chunks + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(rope3d_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p);
-  return launched("rope3d");
+  return rope3d_checked(x, y, B, N, heads, head_dim, grid, theta, (hipStream_t)stream);
+}
+
+size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim) {
+  if (B < 1 || N < 1 || heads < 1 || head_dim != kHeadDim) return 0;
+  return (size_t)B * N * heads * kHeadDim * 2;
 }
 
 wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o, int32_t B,
                             int32_t N, int32_t heads, int32_t head_dim,
                             const wanattn_grid3d* grid, double theta, float scale,
                             wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
-                            void* stream) {
+                            void* workspace, size_t workspace_bytes, void* stream) {
   t_err[0] = 0;
   if (!q || !k || !v || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -242,13 +254,23 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
   if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
     return fail(WANATTN_E_INVALID, "o overlaps an input");
+  if (!workspace) return fail(WANATTN_E_INVALID, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(WANATTN_E_INVALID, "workspace must be 16-byte aligned");
+  if (workspace_bytes < bytes)
+    return fail(WANATTN_E_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, bytes);
+  if (overlap(workspace, bytes, q, bytes) || overlap(workspace, bytes, k, bytes) ||
+      overlap(workspace, bytes, v, bytes) || overlap(workspace, bytes, o, bytes))
+    return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
   WA_TRY(check_lens(B, kv_lens, N, "kv_lens"));
   AttnParams p;
   memset(&p, 0, sizeof p);
   const float2* tab = nullptr;
   WA_TRY(table_for(theta, &tab));
+  // keys rotated once into the workspace; the queries are rotated as the
+  // attention kernel loads them
+  WA_TRY(rope3d_checked(k, workspace, B, N, heads, head_dim, grid, theta, (hipStream_t)stream));
   p.q = (const uint16_t*)q;
-  p.k = (const uint16_t*)k;
+  p.k = (const uint16_t*)workspace;
   p.v = (const uint16_t*)v;
   p.o = (uint16_t*)o;
   p.tab = tab;

@@ -21,8 +21,8 @@ HEAD_DIM = 128
 MAX_POS = 1024
 MAX_LEN_BATCH = 256
 
-EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_cross", "wanattn_prepare",
-           "wanattn_status_string", "wanattn_last_error", "wanattn_version")
+EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wanattn_cross",
+           "wanattn_prepare", "wanattn_status_string", "wanattn_last_error", "wanattn_version")
 
 
 class WanattnError(RuntimeError):
@@ -52,8 +52,11 @@ def load_library(path: str = LIB_PATH):
     G = ctypes.POINTER(Grid3D)
     lib.wanattn_rope3d.argtypes = [P, P, i32, i32, i32, i32, G, f64, P]
     lib.wanattn_rope3d.restype = ctypes.c_int
-    lib.wanattn_self.argtypes = [P, P, P, P, i32, i32, i32, i32, G, f64, f32, ctypes.c_int, i32, P, P]
+    lib.wanattn_self.argtypes = [P, P, P, P, i32, i32, i32, i32, G, f64, f32, ctypes.c_int, i32, P,
+                                 P, ctypes.c_size_t, P]
     lib.wanattn_self.restype = ctypes.c_int
+    lib.wanattn_self_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.wanattn_self_workspace_bytes.restype = ctypes.c_size_t
     lib.wanattn_cross.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, P, P]
     lib.wanattn_cross.restype = ctypes.c_int
     lib.wanattn_prepare.argtypes = [f64]
@@ -129,10 +132,17 @@ def rope3d(x, grid, theta: float = 10000.0, offsets=(0, 0, 0), out=None, stream=
     return out
 
 
+def self_workspace_bytes(B: int, N: int, heads: int, head_dim: int = HEAD_DIM) -> int:
+    return int(load_library().wanattn_self_workspace_bytes(B, N, heads, head_dim))
+
+
 def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = None,
                    block_causal: bool = False, chunk_frames: int = 3, kv_lens=None,
-                   offsets=(0, 0, 0), out=None, stream=None):
-    """softmax(RoPE(q) RoPE(k)^T * scale) v, bidirectional or latent-frame block-causal."""
+                   offsets=(0, 0, 0), out=None, workspace=None, stream=None):
+    """softmax(RoPE(q) RoPE(k)^T * scale) v, bidirectional or latent-frame block-causal.
+
+    workspace: optional GPU tensor of at least self_workspace_bytes(...) bytes
+    (the rotated keys go there); allocated per call when not given."""
     import torch
     lib = load_library()
     if out is None:
@@ -147,9 +157,15 @@ def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = 
     g = _grid(grid, offsets)
     mask = MASK_BLOCK_CAUSAL if block_causal else MASK_NONE
     lens = _lens(kv_lens, B)
+    need = int(lib.wanattn_self_workspace_bytes(B, N, heads, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
     _raise_on(lib.wanattn_self(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, heads, d, ctypes.byref(g),
                                float(theta), float(scale), mask, int(chunk_frames), lens,
-                               _stream(stream)))
+                               _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

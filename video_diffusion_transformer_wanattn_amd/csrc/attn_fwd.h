@@ -140,6 +140,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     else if constexpr (s_ == 2) return st2;
     else return st3;
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
 
   // ---- workgroup -> (batch, head, query tile).  Workgroup w runs on XCD w % 8;
   // give each XCD a contiguous run of tiles so that the concurrent workgroups of
@@ -164,35 +168,51 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   const int nb = 2 * nt;
 
   const size_t row_stride = (size_t)p.heads * kHeadDim;  // elements between tokens
+  const uint32_t rsb = (uint32_t)(row_stride * 2);        // bytes between tokens
   const uint16_t* qbase = p.q + ((size_t)b * p.N * p.heads + head) * kHeadDim;
-  const uint16_t* kbase = p.k + ((size_t)b * p.Nk * p.heads + head) * kHeadDim;
-  const uint16_t* vbase = p.v + ((size_t)b * p.Nk * p.heads + head) * kHeadDim;
+  const char* kbase = (const char*)(p.k + ((size_t)b * p.Nk * p.heads + head) * kHeadDim);
+  const char* vbase = (const char*)(p.v + ((size_t)b * p.Nk * p.heads + head) * kHeadDim);
 
-  // ---- tile loads straight into LDS.  Instruction i of wave w fills 1 KiB =
-  // rows 4(4w+i) .. +3 of the K' and V halves; lane l supplies row
-  // 4(4w+i) + l/16, stored chunk l%16, i.e. global chunk (l%16) ^ swizzle(row).
+  // ---- tile loads straight into LDS.  Instruction i of wave w fills 1 KiB:
+  // rows m = 16w + 4i + l/16 (l = lane), stored chunk l%16 holding global chunk
+  // (l%16) ^ swizzle(m).  K row m holds key k_slot(m) = 16w + 4 swap01(i) + l/16.
+  // The row base is uniform (scalar address), the lane part a fixed 32-bit offset.
   const int ld_row = lane >> 4, ld_chunk = lane & 15;
+  uint32_t koff_ld[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) koff_ld[i] = ld_row * rsb + 16 * (ld_chunk ^ (4 * i + ld_row));
+  const uint32_t voff_ld = ld_row * rsb + 16 * (ld_chunk ^ (4 * ld_row));
   auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {
     char* st = stage(S);
+    if (t * kBN + kBN <= p.Nk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = 4 * wave + i;
-      const int m = 4 * blk + ld_row;
-      const int kkey = min(t * kBN + k_slot(m), p.Nk - 1);
-      const int vkey = min(t * kBN + m, p.Nk - 1);
-      const uint16_t* ks = kbase + (size_t)kkey * row_stride + 8 * (ld_chunk ^ k_swz(m));
-      const uint16_t* vs = vbase + (size_t)vkey * row_stride + 8 * (ld_chunk ^ v_swz(m));
-      __builtin_amdgcn_global_load_lds((const void*)ks,
-                                       (__attribute__((address_space(3))) void*)(st + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)vs, (__attribute__((address_space(3))) void*)(st + kHalfTile + blk * 1024), 16, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int blk = 4 * wave + i;
+        const int krow = t * kBN + 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
+        const int vrow = t * kBN + 16 * wave + 4 * i;
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)krow * rsb + koff_ld[i]),
+                                         (__attribute__((address_space(3))) void*)(st + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(vbase + (size_t)vrow * rsb + voff_ld),
+            (__attribute__((address_space(3))) void*)(st + kHalfTile + blk * 1024), 16, 0, 0);
+      }
+    } else {
+      // last, partial tile: rows beyond the keys repeat the last key
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int blk = 4 * wave + i;
+        const int m = 4 * blk + ld_row;
+        const int kkey = min(t * kBN + k_slot(m), p.Nk - 1);
+        const int vkey = min(t * kBN + m, p.Nk - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(kbase + (size_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m))),
+            (__attribute__((address_space(3))) void*)(st + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(vbase + (size_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m))),
+            (__attribute__((address_space(3))) void*)(st + kHalfTile + blk * 1024), 16, 0, 0);
+      }
     }
   };
-
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
 
   // prefetch the first two tiles while the queries are loaded
   issue_tile(S0{}, 0);
@@ -205,8 +225,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int i = i0 + wave * 64 + qb * 32 + r;
-    const bool valid = i < p.N;
-    const int ic = valid ? i : p.N - 1;
+    const int ic = i < p.N ? i : p.N - 1;
     lim[qb] = row_limit<CAUSAL>(p, kvl, ic);
     int pf = 0, ph = 0, pw = 0;
     if (ROPE) {
@@ -238,53 +257,118 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       for (int j = 0; j < 16; ++j) acc[qb][db][j] = 0.0f;
   float mrun[2] = {-1e30f, -1e30f}, lrun[2] = {0.0f, 0.0f};
 
-  // per-lane pieces of the V transpose-read address
-  const int vg = lane >> 4;         // 16-lane group: hh = vg >> 1, d half = vg & 1
-  const int vu = (lane & 15) >> 2;  // key offset supplied by this lane
-  const int vq = lane & 3;          // d quad supplied by this lane
+  // LDS operand offsets inside a stage.  K: row r (+32 kb), stored chunk
+  // (2 kk + hh) ^ (r & 15).  V (transposed reads): lane (vg, vu, vq) supplies
+  // key 8 (vg>>1) + vu (+ 32 kb + 16 sl + 4 e) and d 32 db + 16 (vg&1) + 4 vq,
+  // whose chunk 4 db + 2 (vg&1) + vq/2 is stored at 4 (db ^ vu) + 2 (vg&1) + vq/2.
+  int koff[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = r * kRowBytes + 16 * ((2 * kk + hh) ^ (r & 15));
+  const int vg = lane >> 4, vu = (lane & 15) >> 2, vq = lane & 3;
+  int voff[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    voff[db] = kHalfTile + (8 * (vg >> 1) + vu) * kRowBytes +
+               16 * (4 * (db ^ vu) + 2 * (vg & 1) + (vq >> 1)) + 8 * (vq & 1);
 
-  // S^T of half kb (32 keys) of the tile in stage S into s
-  auto qk_block = [&](auto S, int kb, floatx16 (&s)[2]) {
+  bf16x8 kop[8];      // K' operands of the next block to score
+  bf16x8 vop[4][2];   // V operands of the block being accumulated
+  float sv[2][16];    // scores of the block being finished (base 2, VGPR copy)
+  floatx16 sacc[2];   // MFMA accumulators of the block being scored
+
+  auto load_kops = [&](auto S, int kb) __attribute__((always_inline)) {
     const char* kt = stage(S) + kb * 32 * kRowBytes;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 a = *(const bf16x8*)(kt + r * kRowBytes + 16 * ((2 * kk + hh) ^ (r & 15)));
-      if (kk == 0) {
-        const floatx16 z = {};
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][0], z, 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][0], z, 0, 0, 0);
-      } else {
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][kk], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][kk], s[1], 0, 0, 0);
+    for (int kk = 0; kk < 8; ++kk) kop[kk] = *(const bf16x8*)(kt + koff[kk]);
+  };
+  auto load_vops = [&](auto S, int kb) __attribute__((always_inline)) {
+    const char* vt = stage(S) + kb * 32 * kRowBytes;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        shortx4 tr[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          tr[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) shortx4*)(vt + (16 * sl + 4 * e) * kRowBytes + voff[db]));
+        // whole-vector casts: assembling this operand element by element was
+        // lowered to a splat of element 0 by the compiler
+        vop[db][sl] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, tr[0]),
+                                              __builtin_bit_cast(bf16x4, tr[1]), 0, 1, 2, 3, 4, 5, 6, 7);
       }
+  };
+  auto qk = [&]() __attribute__((always_inline)) {
+    const floatx16 z = {};
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[0][0], z, 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[1][0], z, 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < 8; ++kk) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
+    }
+  };
+  // exp2(S - m) of the block in sv, row sums, bf16 operands of the PV product
+  auto softmax_exp = [&](bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m = mrun[qb];
+      float sum = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e] - m);
+          const float p1 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1] - m);
+          sum += p0 + p1;
+          pk[e] = pack_bf16x2(p0, p1);
+        }
+        pb[qb][sl] = __builtin_bit_cast(bf16x8, pk);
+      }
+      lrun[qb] += sum;
+    }
+  };
+  auto pv = [&](const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[0][sl], acc[0][db], 0, 0, 0);
+        acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[1][sl], acc[1][db], 0, 0, 0);
+      }
+  };
+  // copy the scored block to VGPRs and take its row max
+  auto take_scores = [&](float (&mx)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sv[qb][e] = sacc[qb][e];
+      float m0 = fmaxf(sv[qb][0], sv[qb][1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(sv[qb][e], sv[qb][e + 1]));
+      mx[qb] = m0;
     }
   };
   // visibility of block j: key of register e is 32 j + 16 (e/8) + 8 hh + e%8
-  auto mask_block = [&](int j, floatx16 (&s)[2]) {
-    if (32 * j + 32 > kv_full) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = 32 * j + 16 * (e >> 3) + 8 * hh + (e & 7);
-          if (key >= lim[qb]) s[qb][e] = -__builtin_inff();
-        }
-    }
-  };
-  auto block_max = [&](floatx16 (&s)[2], float (&mx)[2]) {
+  auto mask_scores = [&](int j, float (&mx)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float m0 = fmaxf(s[qb][0], s[qb][1]);
+      float m0 = -__builtin_inff();
 #pragma unroll
-      for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(s[qb][e], s[qb][e + 1]));
-      mx[qb] = wave_half_max(m0);
+      for (int e = 0; e < 16; ++e) {
+        const int key = 32 * j + 16 * (e >> 3) + 8 * hh + (e & 7);
+        if (key >= lim[qb]) sv[qb][e] = -__builtin_inff();
+        m0 = fmaxf(m0, sv[qb][e]);
+      }
+      mx[qb] = m0;
     }
   };
   // move the running max when it is exceeded by more than kLazyRescale
-  auto update_max = [&](float (&mx)[2]) {
+  auto update_max = [&](float (&mx)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float mnew = fmaxf(mrun[qb], mx[qb]);
+      const float mnew = fmaxf(mrun[qb], wave_half_max(mx[qb]));
       const bool need = mnew > mrun[qb] + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(need)) {
         const float alpha = need ? __builtin_amdgcn_exp2f(mrun[qb] - mnew) : 1.0f;
@@ -297,93 +381,51 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       }
     }
   };
-  // P = exp2(S - m) as bf16 MFMA operands, row sums into lrun
-  auto exp_block = [&](floatx16 (&s)[2], bf16x8 (&pb)[2][2]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m = mrun[qb];
-      float sum = 0.0f;
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(s[qb][8 * sl + 2 * e] - m);
-          const float p1 = __builtin_amdgcn_exp2f(s[qb][8 * sl + 2 * e + 1] - m);
-          sum += p0 + p1;
-          pk[e] = pack_bf16x2(p0, p1);
-        }
-        pb[qb][sl] = __builtin_bit_cast(bf16x8, pk);
-      }
-      lrun[qb] += sum;
-    }
-  };
-  // O^T += V^T P^T for half kb of the tile in stage S
-  auto pv_block = [&](auto S, int kb, const bf16x8 (&pb)[2][2]) {
-    const char* vt = stage(S) + kHalfTile;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        shortx4 tr[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int key = 32 * kb + 16 * sl + 8 * (vg >> 1) + 4 * e + vu;
-          const int chunk = 4 * db + 2 * (vg & 1) + (vq >> 1);
-          const char* addr = vt + key * kRowBytes + 16 * (chunk ^ v_swz(key)) + 8 * (vq & 1);
-          tr[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(addr));
-        }
-        // whole-vector casts: assembling this operand element by element was
-        // lowered to a splat of element 0 by the compiler
-        const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, tr[0]),
-                                                 __builtin_bit_cast(bf16x4, tr[1]), 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][sl], acc[0][db], 0, 0, 0);
-        acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][sl], acc[1][db], 0, 0, 0);
-      }
-    }
+  auto finish_scores = [&](int j) __attribute__((always_inline)) {
+    float mx[2];
+    take_scores(mx);
+    if (32 * j + 32 > kv_full) mask_scores(j, mx);
+    update_max(mx);
   };
 
-  // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored
+  // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored and
+  // finished, K' operands of block 1 loaded
   if (nt > 1) wait_vm<8>();
   else wait_vm<0>();
   tile_barrier();
   if (nt > 2) issue_tile(S2{}, 2);
+  load_kops(S0{}, 0);
+  qk();
+  load_kops(S0{}, 1);
+  finish_scores(0);
 
-  floatx16 s_next[2];
-  float mx[2];
-  qk_block(S0{}, 0, s_next);
-  mask_block(0, s_next);
-  block_max(s_next, mx);
-  update_max(mx);
-
-  // one pipelined step: finish block j (scored in s_next), score block j+1
-  auto block_step = [&](auto S, auto SN, int j, int kb, bool has_next) __attribute__((always_inline)) {
-    floatx16 s_cur[2] = {s_next[0], s_next[1]};
+  // ---- main pipeline.  Block j of tile t (stage S) with j = 2t + kb:
+  //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T  next to  P(j) = exp2(S(j) - m)
+  //   (tile boundary: tile t+1 resident, tile t+3 requested)
+  //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2
+  //   C: scores of block j+1 to VGPRs, row max, running-max update
+  auto block_step = [&](auto S, auto SN, auto SNN, int t, int kb) __attribute__((always_inline)) {
+    const int j = 2 * t + kb;
+    load_vops(S, kb);
     bf16x8 pb[2][2];
-    if (has_next) {
-      if (kb == 0) qk_block(S, 1, s_next);
-      else qk_block(SN, 0, s_next);
-    }
-    exp_block(s_cur, pb);
-    pv_block(S, kb, pb);
-    if (has_next) {
-      mask_block(j + 1, s_next);
-      block_max(s_next, mx);
-      update_max(mx);
-    }
-  };
-  // tile t in stage S: its two blocks; before scoring the first block of tile
-  // t+1 (stage SN) make that tile resident and request tile t+2 into stage SNN
-  auto tile_step = [&](auto S, auto SN, auto SNN, int t) __attribute__((always_inline)) {
-    block_step(S, SN, 2 * t, 0, true);
-    const bool next_tile = t + 1 < nt;
-    if (next_tile) {
+    qk();
+    softmax_exp(pb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb == 0 && t + 1 < nt) {
       if (t + 2 < nt) wait_vm<8>();
       else wait_vm<0>();
       tile_barrier();
       if (t + 3 < nt) issue_tile(SNN, t + 3);
     }
-    block_step(S, SN, 2 * t + 1, 1, next_tile);
+    pv(pb);
+    // block j+2 is half kb of tile t+1 (stage SN)
+    load_kops(SN, kb);
+    __builtin_amdgcn_sched_barrier(0);
+    finish_scores(j + 1);
+  };
+  auto tile_step = [&](auto S, auto SN, auto SNN, int t) __attribute__((always_inline)) {
+    block_step(S, SN, SNN, t, 0);
+    block_step(S, SN, SNN, t, 1);
   };
   for (int t = 0; t < nt; t += 4) {
     tile_step(S0{}, S1{}, S3{}, t);

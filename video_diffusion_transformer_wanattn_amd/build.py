@@ -26,6 +26,9 @@ HIP_FLAGS = [
     # MFMA results in arch VGPRs: the scores are read by VALU right after the
     # product, and the AGPR form made the compiler copy them back and forth
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # no NaN operands reach the kernels' arithmetic (masks use -inf, LDS is
+    # zeroed); this lets row maxima map to v_max3 without NaN canonicalisation
+    "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

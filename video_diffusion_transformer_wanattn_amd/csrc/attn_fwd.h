@@ -133,12 +133,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char st1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char st2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char st3[kTileBytes];
+  // stage as a compile-time constant (main loop) or a run-time index (masked tail)
   auto stage = [&](auto S) __attribute__((always_inline)) -> char* {
-    constexpr int s_ = decltype(S)::value;
-    if constexpr (s_ == 0) return st0;
-    else if constexpr (s_ == 1) return st1;
-    else if constexpr (s_ == 2) return st2;
-    else return st3;
+    if constexpr (std::is_integral_v<decltype(S)>) {
+      const int s_ = S & (kStages - 1);
+      return s_ == 0 ? st0 : (s_ == 1 ? st1 : (s_ == 2 ? st2 : st3));
+    } else {
+      constexpr int s_ = decltype(S)::value;
+      if constexpr (s_ == 0) return st0;
+      else if constexpr (s_ == 1) return st1;
+      else if constexpr (s_ == 2) return st2;
+      else return st3;
+    }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -176,7 +182,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // ---- tile loads straight into LDS.  Instruction i of wave w fills 1 KiB:
   // rows m = 16w + 4i + l/16 (l = lane), stored chunk l%16 holding global chunk
   // (l%16) ^ swizzle(m).  K row m holds key k_slot(m) = 16w + 4 swap01(i) + l/16.
-  // The row base is uniform (scalar address), the lane part a fixed 32-bit offset.
+  // Full tiles: a uniform row base plus a fixed per-lane offset.  The last,
+  // partial tile clamps every row to the last key (those rows are masked).
   const int ld_row = lane >> 4, ld_chunk = lane & 15;
   uint32_t koff_ld[4];
 #pragma unroll
@@ -192,27 +199,35 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
         const int vrow = t * kBN + 16 * wave + 4 * i;
         __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)krow * rsb + koff_ld[i]),
                                          (__attribute__((address_space(3))) void*)(st + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(vbase + (size_t)vrow * rsb + voff_ld),
+        __builtin_amdgcn_global_load_lds((const void*)(vbase + (size_t)vrow * rsb + voff_ld),
             (__attribute__((address_space(3))) void*)(st + kHalfTile + blk * 1024), 16, 0, 0);
       }
     } else {
-      // last, partial tile: rows beyond the keys repeat the last key
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int blk = 4 * wave + i;
         const int m = 4 * blk + ld_row;
         const int kkey = min(t * kBN + k_slot(m), p.Nk - 1);
         const int vkey = min(t * kBN + m, p.Nk - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(kbase + (size_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m))),
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m))),
             (__attribute__((address_space(3))) void*)(st + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(vbase + (size_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m))),
+        __builtin_amdgcn_global_load_lds((const void*)(vbase + (size_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m))),
             (__attribute__((address_space(3))) void*)(st + kHalfTile + blk * 1024), 16, 0, 0);
       }
     }
   };
+
+  // zero every stage once: the look-ahead scoring of the block after the last
+  // one reads a stage that may never have been filled
+#pragma unroll
+  for (int i = 0; i < kTileBytes / 16 / kThreads; ++i) {
+    const int o = 16 * (tid + i * kThreads);
+    *(u32x4*)(st0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4*)(st1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4*)(st2 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4*)(st3 + o) = u32x4{0, 0, 0, 0};
+  }
+  tile_barrier();
 
   // prefetch the first two tiles while the queries are loaded
   issue_tile(S0{}, 0);
@@ -245,6 +260,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       for (int e = 0; e < 4; ++e)
         pk[e] = rotate_pair<ROPE>(raw[e], p.tab, 8 * kk + 4 * hh + e, pf, ph, pw, p.qscale);
       qf[qb][kk] = __builtin_bit_cast(bf16x8, pk);
+      // keep Q in AGPRs: the MFMA reads its B operand from there directly and
+      // the arch VGPRs stay free for the scores and the softmax
+      asm volatile("" : "+a"(qf[qb][kk]));
     }
   }
 
@@ -381,12 +399,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       }
     }
   };
-  auto finish_scores = [&](int j) __attribute__((always_inline)) {
-    float mx[2];
-    take_scores(mx);
-    if (32 * j + 32 > kv_full) mask_scores(j, mx);
-    update_max(mx);
-  };
 
   // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored and
   // finished, K' operands of block 1 loaded
@@ -397,42 +409,68 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   load_kops(S0{}, 0);
   qk();
   load_kops(S0{}, 1);
-  finish_scores(0);
+  {
+    float mx[2];
+    take_scores(mx);
+    if (32 > kv_full) mask_scores(0, mx);
+    update_max(mx);
+  }
 
   // ---- main pipeline.  Block j of tile t (stage S) with j = 2t + kb:
+  //   (first block of a tile: tile t+1 resident, tile t+3 requested)
   //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T  next to  P(j) = exp2(S(j) - m)
-  //   (tile boundary: tile t+1 resident, tile t+3 requested)
-  //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2
-  //   C: scores of block j+1 to VGPRs, row max, running-max update
-  auto block_step = [&](auto S, auto SN, auto SNN, int t, int kb) __attribute__((always_inline)) {
+  //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
+  //      S(j+1) to VGPRs, its mask (tiles that need one) and its row max
+  //   C: running-max update (a rare wave-uniform rescale of O)
+  auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
     const int j = 2 * t + kb;
-    load_vops(S, kb);
-    bf16x8 pb[2][2];
-    qk();
-    softmax_exp(pb);
-    __builtin_amdgcn_sched_barrier(0);
     if (kb == 0 && t + 1 < nt) {
       if (t + 2 < nt) wait_vm<8>();
       else wait_vm<0>();
       tile_barrier();
       if (t + 3 < nt) issue_tile(SNN, t + 3);
     }
-    pv(pb);
-    // block j+2 is half kb of tile t+1 (stage SN)
-    load_kops(SN, kb);
     __builtin_amdgcn_sched_barrier(0);
-    finish_scores(j + 1);
+    load_vops(S, kb);
+    bf16x8 pb[2][2];
+    qk();
+    softmax_exp(pb);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(pb);
+    load_kops(SN, kb);  // block j+2 is half kb of tile t+1 (stage SN)
+    float mx[2];
+    take_scores(mx);
+    if constexpr (decltype(MASKED)::value) mask_scores(j + 1, mx);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    update_max(mx);
   };
-  auto tile_step = [&](auto S, auto SN, auto SNN, int t) __attribute__((always_inline)) {
-    block_step(S, SN, SNN, t, 0);
-    block_step(S, SN, SNN, t, 1);
+  using NoMask = std::integral_constant<bool, false>;
+  using Mask = std::integral_constant<bool, true>;
+  // Block j+1 (scored in step j) needs the element mask iff 32 (j+1) + 32 > kv_full,
+  // i.e. from block jm = kv_full / 32 on.  Whole tiles whose steps score only
+  // earlier blocks run in the unrolled loop with compile-time stages; the rest
+  // (the last tile or two, or the chunk a causal query tile straddles) run in a
+  // loop with run-time stages.
+  const int jm = kv_full / 32;
+  const int tm = min(nt, max(0, (jm - 1) / 2));
+  auto tile_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t) __attribute__((always_inline)) {
+    block_step(S, SN, SNN, MASKED, t, 0);
+    block_step(S, SN, SNN, MASKED, t, 1);
   };
-  for (int t = 0; t < nt; t += 4) {
-    tile_step(S0{}, S1{}, S3{}, t);
-    if (t + 1 < nt) tile_step(S1{}, S2{}, S0{}, t + 1);
-    if (t + 2 < nt) tile_step(S2{}, S3{}, S1{}, t + 2);
-    if (t + 3 < nt) tile_step(S3{}, S0{}, S2{}, t + 3);
+  int t = 0;
+  for (; t + 4 <= tm; t += 4) {
+    tile_step(S0{}, S1{}, S3{}, NoMask{}, t);
+    tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 1);
+    tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 2);
+    tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 3);
   }
+  for (; t < nt; ++t) tile_step(t, t + 1, t + 3, Mask{}, t);
 
   // ---- epilogue: O = O^T / l, bf16; lane holds d = 32 db + 8 g4 + 4 hh + 0..3
 #pragma unroll

@@ -35,10 +35,12 @@
 // free of bank conflicts.
 //
 // Softmax is in base 2: the query is multiplied by scale * log2(e) when it is
-// loaded, so p = exp2(s - m) maps to v_exp_f32.  The running max is only moved
-// when a row's block max exceeds it by more than 8 (p <= 256 in between), which
-// makes the O rescale rare; the result is the same softmax (the final division
-// by the running sum uses the same reference point).
+// loaded, so p = exp2(s - m) maps to v_exp_f32, and the subtraction of the row
+// reference m is folded into the QK^T product as one more MFMA k-step (a
+// K-side constant 1 against -m on the Q side, as two bf16 terms).  The
+// reference is only moved when a row's shifted block max exceeds 8 (p <= 256 in
+// between), which makes the O rescale rare; the result is the same softmax (the
+// final division by the running sum uses the same reference point).
 #pragma once
 
 #include <type_traits>
@@ -273,7 +275,27 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[qb][db][j] = 0.0f;
-  float mrun[2] = {-1e30f, -1e30f}, lrun[2] = {0.0f, 0.0f};
+  // Running softmax reference per query row, kept as a bias b = -m added to the
+  // scores inside the QK^T product: one extra MFMA k-step multiplies the K-side
+  // constant (1, 1) with the Q-side (hi, lo), the bias split into two bf16
+  // terms (b = hi + lo exactly in fp32, ~16 significant bits).  The scores come
+  // out of the product already shifted, and p = exp2(s) needs no subtraction.
+  float bias[2] = {0.0f, 0.0f}, lrun[2] = {0.0f, 0.0f};
+  bf16x8 qbias[2];
+  const bf16x8 kbias = __builtin_bit_cast(bf16x8, u32x4{hh == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u});
+  auto set_bias = [&](int qb, float b) __attribute__((always_inline)) {
+    const __bf16 hi = (__bf16)b;
+    const __bf16 lo = (__bf16)(b - (float)hi);
+    bias[qb] = (float)hi + (float)lo;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v;
+    v[0] = hi;
+    v[1] = lo;
+    const uint32_t w = hh == 0 ? __builtin_bit_cast(uint32_t, v) : 0u;
+    qbias[qb] = __builtin_bit_cast(bf16x8, u32x4{w, 0u, 0u, 0u});
+  };
+  set_bias(0, 0.0f);
+  set_bias(1, 0.0f);
 
   // LDS operand offsets inside a stage.  K: row r (+32 kb), stored chunk
   // (2 kk + hh) ^ (r & 15).  V (transposed reads): lane (vg, vu, vq) supplies
@@ -318,27 +340,26 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   };
   auto qk = [&]() __attribute__((always_inline)) {
     const floatx16 z = {};
-    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[0][0], z, 0, 0, 0);
-    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[1][0], z, 0, 0, 0);
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias, qbias[0], z, 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias, qbias[1], z, 0, 0, 0);
 #pragma unroll
-    for (int kk = 1; kk < 8; ++kk) {
+    for (int kk = 0; kk < 8; ++kk) {
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], sacc[0], 0, 0, 0);
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
     }
   };
-  // exp2(S - m) of the block in sv, row sums, bf16 operands of the PV product
+  // exp2 of the shifted scores in sv, row sums, bf16 operands of the PV product
   auto softmax_exp = [&](bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float m = mrun[qb];
       float sum = 0.0f;
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e] - m);
-          const float p1 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1] - m);
+          const float p0 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e]);
+          const float p1 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1]);
           sum += p0 + p1;
           pk[e] = pack_bf16x2(p0, p1);
         }
@@ -382,20 +403,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       mx[qb] = m0;
     }
   };
-  // move the running max when it is exceeded by more than kLazyRescale
-  auto update_max = [&](float (&mx)[2]) __attribute__((always_inline)) {
+  // Move the reference of a row when its shifted block max exceeds
+  // kLazyRescale (rare after the first blocks): b -= max, O and l scaled by
+  // 2^(b_new - b_old), the block's scores shifted alike.  One wave-uniform
+  // branch for both row blocks.
+  auto update_bias = [&](float (&mx)[2]) __attribute__((always_inline)) {
+    const float m0 = wave_half_max(mx[0]), m1 = wave_half_max(mx[1]);
+    const bool n0 = m0 > kLazyRescale, n1 = m1 > kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(n0 || n1)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float mnew = fmaxf(mrun[qb], wave_half_max(mx[qb]));
-      const bool need = mnew > mrun[qb] + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(mrun[qb] - mnew) : 1.0f;
-        mrun[qb] = need ? mnew : mrun[qb];
+      for (int qb = 0; qb < 2; ++qb) {
+        const bool need = qb == 0 ? n0 : n1;
+        const float old = bias[qb];
+        set_bias(qb, need ? old - (qb == 0 ? m0 : m1) : old);
+        const float delta = bias[qb] - old;
+        const float alpha = __builtin_amdgcn_exp2f(delta);
         lrun[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[qb][db][e] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sv[qb][e] += delta;
       }
     }
   };
@@ -410,18 +439,25 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   qk();
   load_kops(S0{}, 1);
   {
+    // block 0 was scored with b = 0; its row max becomes the first reference
+    // (every row sees key 0, so the max is finite; O and l are still zero)
     float mx[2];
     take_scores(mx);
     if (32 > kv_full) mask_scores(0, mx);
-    update_max(mx);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      set_bias(qb, -wave_half_max(mx[qb]));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sv[qb][e] += bias[qb];
+    }
   }
 
   // ---- main pipeline.  Block j of tile t (stage S) with j = 2t + kb:
   //   (first block of a tile: tile t+1 resident, tile t+3 requested)
-  //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T  next to  P(j) = exp2(S(j) - m)
+  //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T + b  next to  P(j) = exp2(S(j) + b)
   //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
   //      S(j+1) to VGPRs, its mask (tiles that need one) and its row max
-  //   C: running-max update (a rare wave-uniform rescale of O)
+  //   C: reference update (a rare wave-uniform rescale of O)
   auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
     const int j = 2 * t + kb;
     if (kb == 0 && t + 1 < nt) {
@@ -431,24 +467,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       if (t + 3 < nt) issue_tile(SNN, t + 3);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // phase A (V operands of block j for phase B, QK^T of block j+1, exp of block j)
     load_vops(S, kb);
     bf16x8 pb[2][2];
     qk();
     softmax_exp(pb);
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-    }
     __builtin_amdgcn_sched_barrier(0);
+    // phase B (K' operands of block j+2 = half kb of tile t+1 in stage SN, PV of
+    // block j, copy and row max of block j+1)
+    load_kops(SN, kb);
     pv(pb);
-    load_kops(SN, kb);  // block j+2 is half kb of tile t+1 (stage SN)
     float mx[2];
     take_scores(mx);
     if constexpr (decltype(MASKED)::value) mask_scores(j + 1, mx);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-    }
     __builtin_amdgcn_sched_barrier(0);
-    update_max(mx);
+    update_bias(mx);
   };
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;

@@ -60,7 +60,7 @@ constexpr int kTileBytes = 2 * kHalfTile;      // 32 KiB
 constexpr int kStages = 4;
 constexpr int kLdsBytes = kStages * kTileBytes;  // 128 KiB of 160
 constexpr int kLoadsPerTile = 8;               // global_load_lds per thread per tile (4 K + 4 V)
-constexpr float kLazyRescale = 8.0f;           // log2 units
+constexpr float kLazySum = 65536.0f;           // lane partial block sum that moves the reference
 
 struct AttnParams {
   const uint16_t* q;
@@ -348,25 +348,32 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
     }
   };
-  // exp2 of the shifted scores in sv, row sums, bf16 operands of the PV product
-  auto softmax_exp = [&](bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+  // exp2 of the shifted scores in sv, bf16 operands of the PV product, and
+  // this lane's block sums of exactly those bf16 values (dot with (1, 1))
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto softmax_exp_row = [&](int qb, bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float sum = 0.0f;
+    for (int sl = 0; sl < 2; ++sl) {
+      u32x4 pk;
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e]);
-          const float p1 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1]);
-          sum += p0 + p1;
-          pk[e] = pack_bf16x2(p0, p1);
-        }
-        pb[qb][sl] = __builtin_bit_cast(bf16x8, pk);
+      for (int e = 0; e < 4; ++e) {
+        // the word is summed before it enters the vector: taking the pair back
+        // out of the vector was miscompiled (every sum read element 0)
+        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e]),
+                                       __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1]));
+        if (e & 1) s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, s1, false);
+        else s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, s0, false);
+        pk[e] = w;
       }
-      lrun[qb] += sum;
+      pb[qb][sl] = __builtin_bit_cast(bf16x8, pk);
     }
+    bsum[qb] = s0 + s1;
+  };
+  auto softmax_exp = [&](bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
+    softmax_exp_row(0, pb, bsum);
+    softmax_exp_row(1, pb, bsum);
   };
   auto pv = [&](const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -377,55 +384,55 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
         acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[1][sl], acc[1][db], 0, 0, 0);
       }
   };
-  // copy the scored block to VGPRs and take its row max
-  auto take_scores = [&](float (&mx)[2]) __attribute__((always_inline)) {
+  // copy the scored block to VGPRs
+  auto take_scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sv[qb][e] = sacc[qb][e];
-      float m0 = fmaxf(sv[qb][0], sv[qb][1]);
-#pragma unroll
-      for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(sv[qb][e], sv[qb][e + 1]));
-      mx[qb] = m0;
-    }
   };
   // visibility of block j: key of register e is 32 j + 16 (e/8) + 8 hh + e%8
-  auto mask_scores = [&](int j, float (&mx)[2]) __attribute__((always_inline)) {
+  auto mask_scores = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float m0 = -__builtin_inff();
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = 32 * j + 16 * (e >> 3) + 8 * hh + (e & 7);
         if (key >= lim[qb]) sv[qb][e] = -__builtin_inff();
-        m0 = fmaxf(m0, sv[qb][e]);
       }
-      mx[qb] = m0;
-    }
   };
-  // Move the reference of a row when its shifted block max exceeds
-  // kLazyRescale (rare after the first blocks): b -= max, O and l scaled by
-  // 2^(b_new - b_old), the block's scores shifted alike.  One wave-uniform
-  // branch for both row blocks.
-  auto update_bias = [&](float (&mx)[2]) __attribute__((always_inline)) {
-    const float m0 = wave_half_max(mx[0]), m1 = wave_half_max(mx[1]);
-    const bool n0 = m0 > kLazyRescale, n1 = m1 > kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(n0 || n1)) {
+  auto row_max = [&](int qb) __attribute__((always_inline)) -> float {
+    float m0 = fmaxf(sv[qb][0], sv[qb][1]);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const bool need = qb == 0 ? n0 : n1;
-        const float old = bias[qb];
-        set_bias(qb, need ? old - (qb == 0 ? m0 : m1) : old);
-        const float delta = bias[qb] - old;
-        const float alpha = __builtin_amdgcn_exp2f(delta);
-        lrun[qb] *= alpha;
+    for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(sv[qb][e], sv[qb][e + 1]));
+    return wave_half_max(m0);
+  };
+  // Lazy reference (rare after the first blocks).  The probabilities of block
+  // j were taken against the current reference; when a lane's partial block
+  // sum exceeds kLazySum (some p above 2^12, or an overflow to inf), every row
+  // whose block max lies above its reference moves the reference to that max:
+  // O and l are scaled by 2^(b_new - b_old), block j's probabilities are taken
+  // again, and the scores of block j+1 (already formed against the old
+  // reference) are shifted alike.  One wave-uniform branch for both row blocks.
+  auto move_reference = [&](bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m = row_max(qb);
+      const float old = bias[qb];
+      set_bias(qb, m > 0.0f ? old - m : old);
+      const float delta = bias[qb] - old;
+      const float alpha = __builtin_amdgcn_exp2f(delta);
+      lrun[qb] *= alpha;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[qb][db][e] *= alpha;
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sv[qb][e] += delta;
+        for (int e = 0; e < 16; ++e) acc[qb][db][e] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sv[qb][e] += delta;
+        sacc[qb][e] += delta;
       }
+      softmax_exp_row(qb, pb, bsum);
     }
   };
 
@@ -441,12 +448,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   {
     // block 0 was scored with b = 0; its row max becomes the first reference
     // (every row sees key 0, so the max is finite; O and l are still zero)
-    float mx[2];
-    take_scores(mx);
-    if (32 > kv_full) mask_scores(0, mx);
+    take_scores();
+    if (32 > kv_full) mask_scores(0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      set_bias(qb, -wave_half_max(mx[qb]));
+      set_bias(qb, -row_max(qb));
 #pragma unroll
       for (int e = 0; e < 16; ++e) sv[qb][e] += bias[qb];
     }
@@ -455,9 +461,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // ---- main pipeline.  Block j of tile t (stage S) with j = 2t + kb:
   //   (first block of a tile: tile t+1 resident, tile t+3 requested)
   //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T + b  next to  P(j) = exp2(S(j) + b)
+  //      and the block sums of P(j)
+  //   (rare, wave-uniform: move the reference, see move_reference)
   //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
-  //      S(j+1) to VGPRs, its mask (tiles that need one) and its row max
-  //   C: reference update (a rare wave-uniform rescale of O)
+  //      S(j+1) to VGPRs and its mask (tiles that need one)
   auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
     const int j = 2 * t + kb;
     if (kb == 0 && t + 1 < nt) {
@@ -470,18 +477,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     // phase A (V operands of block j for phase B, QK^T of block j+1, exp of block j)
     load_vops(S, kb);
     bf16x8 pb[2][2];
+    float bsum[2];
     qk();
-    softmax_exp(pb);
+    softmax_exp(pb, bsum);
     __builtin_amdgcn_sched_barrier(0);
+    if (__builtin_amdgcn_ballot_w64(fmaxf(bsum[0], bsum[1]) > kLazySum)) move_reference(pb, bsum);
+    lrun[0] += bsum[0];
+    lrun[1] += bsum[1];
     // phase B (K' operands of block j+2 = half kb of tile t+1 in stage SN, PV of
-    // block j, copy and row max of block j+1)
+    // block j, copy of block j+1)
     load_kops(SN, kb);
     pv(pb);
-    float mx[2];
-    take_scores(mx);
-    if constexpr (decltype(MASKED)::value) mask_scores(j + 1, mx);
-    __builtin_amdgcn_sched_barrier(0);
-    update_bias(mx);
+    take_scores();
+    if constexpr (decltype(MASKED)::value) mask_scores(j + 1);
   };
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;

@@ -19,11 +19,13 @@
 // Per 32-key block and wave (two blocks per tile):
 //   S^T (keys x queries) = K' Q'^T   v_mfma_f32_32x32x16_bf16, 2 x 8 issues
 //   online softmax on S^T: a lane holds 16 scores of ONE query per block, so
-//   row max and row sum are in-lane plus one permlane32 swap
+//   row sums are in-lane (plus one permlane32 swap at the end)
 //   O^T (d x queries) += V^T P^T     2 x 4 x 2 issues; P stays in registers
 // The loop is software-pipelined over blocks: the QK^T products of block j+1
-// are issued next to the exp/convert work of block j, and the PV products of
-// block j next to the row max of block j+1.
+// are issued next to the exp work of keys 16..31 of block j, and the PV
+// products of block j next to the exp work of keys 0..15 of block j+1, so each
+// MFMA has a few independent VALU instructions beside it (one wave per SIMD:
+// the VALU work only overlaps the MFMA pipe when it is spread out like this).
 //
 // Key order inside a 32-key MFMA block is free (the contraction is a sum), so
 // K rows sit in LDS permuted (bits 2 and 3 of the key index swapped): the S^T
@@ -38,9 +40,10 @@
 // loaded, so p = exp2(s - m) maps to v_exp_f32, and the subtraction of the row
 // reference m is folded into the QK^T product as one more MFMA k-step (a
 // K-side constant 1 against -m on the Q side, as two bf16 terms).  The
-// reference is only moved when a row's shifted block max exceeds 8 (p <= 256 in
-// between), which makes the O rescale rare; the result is the same softmax (the
-// final division by the running sum uses the same reference point).
+// reference starts at the max of the first block and is only moved when a
+// lane's block sum of p exceeds 2^16 (some p above 2^12, or an overflow), which
+// makes the O rescale rare; the result is the same softmax (the final division
+// by the running sum uses the same reference point).
 #pragma once
 
 #include <type_traits>
@@ -126,6 +129,14 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// 16 bytes per lane from gbase + voff into LDS at lds + 16 * lane.  Written as
+// asm so that the compiler does not track the LDS write (the kernel waits for
+// these loads itself with vmcnt and a barrier)
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+
 template <bool ROPE, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // one LDS object per stage: accesses to different stages then carry distinct
@@ -192,29 +203,27 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   for (int i = 0; i < 4; ++i) koff_ld[i] = ld_row * rsb + 16 * (ld_chunk ^ (4 * i + ld_row));
   const uint32_t voff_ld = ld_row * rsb + 16 * (ld_chunk ^ (4 * ld_row));
   auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {
-    char* st = stage(S);
+    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
+    const char* kt = kbase + (size_t)t * kBN * rsb;
+    const char* vt = vbase + (size_t)t * kBN * rsb;
     if (t * kBN + kBN <= p.Nk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int blk = 4 * wave + i;
-        const int krow = t * kBN + 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
-        const int vrow = t * kBN + 16 * wave + 4 * i;
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)krow * rsb + koff_ld[i]),
-                                         (__attribute__((address_space(3))) void*)(st + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase + (size_t)vrow * rsb + voff_ld),
-            (__attribute__((address_space(3))) void*)(st + kHalfTile + blk * 1024), 16, 0, 0);
+        const int krow = 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
+        const int vrow = 16 * wave + 4 * i;
+        dma16(kt + (size_t)krow * rsb, koff_ld[i], st + blk * 1024);
+        dma16(vt + (size_t)vrow * rsb, voff_ld, st + kHalfTile + blk * 1024);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int blk = 4 * wave + i;
         const int m = 4 * blk + ld_row;
-        const int kkey = min(t * kBN + k_slot(m), p.Nk - 1);
-        const int vkey = min(t * kBN + m, p.Nk - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m))),
-            (__attribute__((address_space(3))) void*)(st + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase + (size_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m))),
-            (__attribute__((address_space(3))) void*)(st + kHalfTile + blk * 1024), 16, 0, 0);
+        const int kkey = min(t * kBN + k_slot(m), p.Nk - 1) - t * kBN;
+        const int vkey = min(t * kBN + m, p.Nk - 1) - t * kBN;
+        dma16(kt, (uint32_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m)), st + blk * 1024);
+        dma16(vt, (uint32_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m)), st + kHalfTile + blk * 1024);
       }
     }
   };
@@ -315,28 +324,29 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   bf16x8 vop[4][2];   // V operands of the block being accumulated
   float sv[2][16];    // scores of the block being finished (base 2, VGPR copy)
   floatx16 sacc[2];   // MFMA accumulators of the block being scored
+  bf16x8 pcar[2];     // P of keys 0..15 of the block being finished, taken one phase early
+  float scar[2];      // and this lane's sums of them
 
   auto load_kops = [&](auto S, int kb) __attribute__((always_inline)) {
     const char* kt = stage(S) + kb * 32 * kRowBytes;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) kop[kk] = *(const bf16x8*)(kt + koff[kk]);
   };
-  auto load_vops = [&](auto S, int kb) __attribute__((always_inline)) {
+  // single operand reads, for the hand-ordered block step
+  auto load_kop = [&](auto S, int kb, int kk) __attribute__((always_inline)) {
+    kop[kk] = *(const bf16x8*)(stage(S) + kb * 32 * kRowBytes + koff[kk]);
+  };
+  auto load_vop = [&](auto S, int kb, int db, int sl) __attribute__((always_inline)) {
     const char* vt = stage(S) + kb * 32 * kRowBytes;
+    shortx4 tr[2];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        shortx4 tr[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          tr[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) shortx4*)(vt + (16 * sl + 4 * e) * kRowBytes + voff[db]));
-        // whole-vector casts: assembling this operand element by element was
-        // lowered to a splat of element 0 by the compiler
-        vop[db][sl] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, tr[0]),
-                                              __builtin_bit_cast(bf16x4, tr[1]), 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+    for (int e = 0; e < 2; ++e)
+      tr[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) shortx4*)(vt + (16 * sl + 4 * e) * kRowBytes + voff[db]));
+    // whole-vector casts: assembling this operand element by element was
+    // lowered to a splat of element 0 by the compiler
+    vop[db][sl] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, tr[0]), __builtin_bit_cast(bf16x4, tr[1]),
+                                          0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto qk = [&]() __attribute__((always_inline)) {
     const floatx16 z = {};
@@ -348,41 +358,30 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
     }
   };
-  // exp2 of the shifted scores in sv, bf16 operands of the PV product, and
-  // this lane's block sums of exactly those bf16 values (dot with (1, 1))
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // exp2 of the shifted scores in sv: bf16 operands of the PV product and this
+  // lane's fp32 block sums.  One pair of probabilities (keys 16 sl + 2 e, + 1)
+  // of row block qb: packed word into pk[e], sum into acc2[e & 1].  (Plain adds:
+  // the dot-product VALU instructions wait for the MFMA pipe to drain.)
+  auto exp_pair = [&](int qb, int sl, int e, u32x4& pk, float (&acc2)[2]) __attribute__((always_inline)) {
+    const float p0 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e]);
+    const float p1 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1]);
+    acc2[e & 1] += p0 + p1;
+    pk[e] = pack_bf16x2(p0, p1);
+  };
+  // (half sl of the block: keys 16 sl .. 16 sl + 15, registers 8 sl .. 8 sl + 7)
+  auto exp_half = [&](int qb, int sl, bf16x8& out, float& sum) __attribute__((always_inline)) {
+    float acc2[2] = {0.0f, 0.0f};
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) exp_pair(qb, sl, e, pk, acc2);
+    out = __builtin_bit_cast(bf16x8, pk);
+    sum = acc2[0] + acc2[1];
+  };
   auto softmax_exp_row = [&](int qb, bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      u32x4 pk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // the word is summed before it enters the vector: taking the pair back
-        // out of the vector was miscompiled (every sum read element 0)
-        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e]),
-                                       __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1]));
-        if (e & 1) s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, s1, false);
-        else s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, s0, false);
-        pk[e] = w;
-      }
-      pb[qb][sl] = __builtin_bit_cast(bf16x8, pk);
-    }
-    bsum[qb] = s0 + s1;
-  };
-  auto softmax_exp = [&](bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
-    softmax_exp_row(0, pb, bsum);
-    softmax_exp_row(1, pb, bsum);
-  };
-  auto pv = [&](const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[0][sl], acc[0][db], 0, 0, 0);
-        acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[1][sl], acc[1][db], 0, 0, 0);
-      }
+    float h0, h1;
+    exp_half(qb, 0, pb[qb][0], h0);
+    exp_half(qb, 1, pb[qb][1], h1);
+    bsum[qb] = h0 + h1;
   };
   // copy the scored block to VGPRs
   auto take_scores = [&]() __attribute__((always_inline)) {
@@ -455,16 +454,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       set_bias(qb, -row_max(qb));
 #pragma unroll
       for (int e = 0; e < 16; ++e) sv[qb][e] += bias[qb];
+      exp_half(qb, 0, pcar[qb], scar[qb]);
     }
   }
 
   // ---- main pipeline.  Block j of tile t (stage S) with j = 2t + kb:
   //   (first block of a tile: tile t+1 resident, tile t+3 requested)
-  //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T + b  next to  P(j) = exp2(S(j) + b)
-  //      and the block sums of P(j)
+  //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T + b  next to  P(j) = exp2(S(j))
+  //      for keys 16..31 and the block sums of P(j)
   //   (rare, wave-uniform: move the reference, see move_reference)
   //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
-  //      S(j+1) to VGPRs and its mask (tiles that need one)
+  //      S(j+1) to VGPRs, its mask (tiles that need one) and P(j+1) for keys 0..15
+  // so that both phases carry about the same exp work beside their MFMAs
+  // The step is written as small groups fenced by scheduling barriers, each an
+  // MFMA pair plus the VALU and LDS work meant to run beside it: an MFMA leaves
+  // the VALU only part of its cycles, so that work must be spread evenly.
   auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
     const int j = 2 * t + kb;
     if (kb == 0 && t + 1 < nt) {
@@ -474,22 +478,74 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       if (t + 3 < nt) issue_tile(SNN, t + 3);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // phase A (V operands of block j for phase B, QK^T of block j+1, exp of block j)
-    load_vops(S, kb);
+    // ---- phase A: S(j+1) = K'(j+1) Q'^T + b; P(j) for keys 16..31; V(j) operands
+    // lgkmcnt(0), as an instruction the compiler accounts for: the K' operands
+    // read during the previous phase are complete here, so no drain is needed
+    // later in this phase, after the V reads below have been issued
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    u32x4 pk1[2];
+    float h1[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    {
+      const floatx16 z = {};
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias, qbias[0], z, 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias, qbias[1], z, 0, 0, 0);
+      load_vop(S, kb, 0, 0);
+      load_vop(S, kb, 0, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
+      exp_pair(kk >> 2, 1, kk & 3, pk1[kk >> 2], h1[kk >> 2]);
+      // keep the packed word here: it is only read after the check below,
+      // and would otherwise be sunk past it
+      asm volatile("" : "+v"(pk1[kk >> 2][kk & 3]));
+      if (kk < 6) load_vop(S, kb, 1 + kk / 2, kk & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     bf16x8 pb[2][2];
     float bsum[2];
-    qk();
-    softmax_exp(pb, bsum);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      pb[qb][0] = pcar[qb];
+      pb[qb][1] = __builtin_bit_cast(bf16x8, pk1[qb]);
+      bsum[qb] = scar[qb] + (h1[qb][0] + h1[qb][1]);
+    }
     if (__builtin_amdgcn_ballot_w64(fmaxf(bsum[0], bsum[1]) > kLazySum)) move_reference(pb, bsum);
     lrun[0] += bsum[0];
     lrun[1] += bsum[1];
-    // phase B (K' operands of block j+2 = half kb of tile t+1 in stage SN, PV of
-    // block j, copy of block j+1)
-    load_kops(SN, kb);
-    pv(pb);
-    take_scores();
-    if constexpr (decltype(MASKED)::value) mask_scores(j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase B: O += V(j)^T P(j)^T; K'(j+2) operands; S(j+1) to VGPRs (and
+    // its mask); P(j+1) for keys 0..15
+    u32x4 pk0[2];
+    float h0[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int db = g >> 1, sl = g & 1;
+      acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[0][sl], acc[0][db], 0, 0, 0);
+      acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[1][sl], acc[1][db], 0, 0, 0);
+      load_kop(SN, kb, g);
+      if (g == 0) {
+        take_scores();
+        if constexpr (decltype(MASKED)::value) mask_scores(j + 1);
+      } else {
+        // pairs (qb, e) = (0, 0..3), (1, 0..3) over groups 1..7, two in group 1
+        const int pr = g == 1 ? 0 : g;
+        exp_pair(pr >> 2, 0, pr & 3, pk0[pr >> 2], h0[pr >> 2]);
+        asm volatile("" : "+v"(pk0[pr >> 2][pr & 3]), "+v"(h0[pr >> 2][pr & 1]));
+        if (g == 1) {
+          exp_pair(0, 0, 1, pk0[0], h0[0]);
+          asm volatile("" : "+v"(pk0[0][1]), "+v"(h0[0][1]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      pcar[qb] = __builtin_bit_cast(bf16x8, pk0[qb]);
+      scar[qb] = h0[qb][0] + h0[qb][1];
+    }
   };
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;

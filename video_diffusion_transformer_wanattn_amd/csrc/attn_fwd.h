@@ -202,19 +202,26 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) koff_ld[i] = ld_row * rsb + 16 * (ld_chunk ^ (4 * i + ld_row));
   const uint32_t voff_ld = ld_row * rsb + 16 * (ld_chunk ^ (4 * ld_row));
+  // a tile known to hold kBN keys
+  auto issue_full_tile = [&](auto S, int t) __attribute__((always_inline)) {
+    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
+    const char* kt = kbase + (size_t)t * kBN * rsb;
+    const char* vt = vbase + (size_t)t * kBN * rsb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = 4 * wave + i;
+      const int krow = 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
+      const int vrow = 16 * wave + 4 * i;
+      dma16(kt + (size_t)krow * rsb, koff_ld[i], st + blk * 1024);
+      dma16(vt + (size_t)vrow * rsb, voff_ld, st + kHalfTile + blk * 1024);
+    }
+  };
   auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {
     const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
     const char* kt = kbase + (size_t)t * kBN * rsb;
     const char* vt = vbase + (size_t)t * kBN * rsb;
     if (t * kBN + kBN <= p.Nk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int blk = 4 * wave + i;
-        const int krow = 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
-        const int vrow = 16 * wave + 4 * i;
-        dma16(kt + (size_t)krow * rsb, koff_ld[i], st + blk * 1024);
-        dma16(vt + (size_t)vrow * rsb, voff_ld, st + kHalfTile + blk * 1024);
-      }
+      issue_full_tile(S, t);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -469,9 +476,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // The step is written as small groups fenced by scheduling barriers, each an
   // MFMA pair plus the VALU and LDS work meant to run beside it: an MFMA leaves
   // the VALU only part of its cycles, so that work must be spread evenly.
+  // MASKED steps (the tail loop) check at run time which tiles exist; the
+  // others (the unrolled main loop) only run where tiles t+1..t+3 exist and
+  // t+3 is full, and need no element mask.
   auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
     const int j = 2 * t + kb;
-    if (kb == 0 && t + 1 < nt) {
+    if constexpr (!decltype(MASKED)::value) {
+      if (kb == 0) {
+        wait_vm<8>();
+        tile_barrier();
+        issue_full_tile(SNN, t + 3);
+      }
+    } else if (kb == 0 && t + 1 < nt) {
       if (t + 2 < nt) wait_vm<8>();
       else wait_vm<0>();
       tile_barrier();
@@ -551,11 +567,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   using Mask = std::integral_constant<bool, true>;
   // Block j+1 (scored in step j) needs the element mask iff 32 (j+1) + 32 > kv_full,
   // i.e. from block jm = kv_full / 32 on.  Whole tiles whose steps score only
-  // earlier blocks run in the unrolled loop with compile-time stages; the rest
-  // (the last tile or two, or the chunk a causal query tile straddles) run in a
-  // loop with run-time stages.
+  // earlier blocks, and for which tile t+3 exists and is full, run in the
+  // unrolled loop with compile-time stages; the rest (the last few tiles, or
+  // the chunk a causal query tile straddles) run in a loop with run-time stages.
   const int jm = kv_full / 32;
-  const int tm = min(nt, max(0, (jm - 1) / 2));
+  const int tm = max(0, min(min(nt, (jm - 1) / 2), p.Nk / kBN - 3));
   auto tile_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t) __attribute__((always_inline)) {
     block_step(S, SN, SNN, MASKED, t, 0);
     block_step(S, SN, SNN, MASKED, t, 1);

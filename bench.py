@@ -64,7 +64,7 @@ def cpu_baseline(wl, t, threads):
     from video_diffusion_transformer_wanattn_amd import seeded
 
     grid = (wl.F, wl.H, wl.W)
-    R1, R2 = 32, 160
+    R1, R2 = 64, 448
     rows1 = seeded.sample_rows(wl.N, R1, seed=1)
     rows2 = seeded.sample_rows(wl.N, R2, seed=2)
     kw = dict(theta=10000.0, block_causal=wl.block_causal, chunk_frames=wl.chunk_frames,

@@ -62,6 +62,7 @@ def call_self(lib, q=A, k=B_, v=C, o=O, B=1, N=24, heads=2, d=128, grid=None, th
     (dict(N=0), wa.E_INVALID),
     (dict(heads=0), wa.E_INVALID),
     (dict(d=64), wa.E_UNSUPPORTED),
+    (dict(heads=65537, N=24), wa.E_UNSUPPORTED),                  # above WANATTN_MAX_HEADS
     (dict(N=25), wa.E_INVALID),                                   # N != F*H*W
     (dict(grid=None, N=24), wa.E_INVALID),
     (dict(theta=0.0), wa.E_INVALID),
@@ -111,6 +112,7 @@ def test_cross_rejects(lib):
     assert call(v=None) == wa.E_INVALID
     assert call(M=0) == wa.E_INVALID
     assert call(d=96) == wa.E_UNSUPPORTED
+    assert call(heads=65537) == wa.E_UNSUPPORTED
     assert call(o=B_) == wa.E_INVALID
     assert call(lens=(ctypes.c_int32 * 1)(9)) == wa.E_INVALID
     assert call(lens=(ctypes.c_int32 * 1)(0)) == wa.E_INVALID

@@ -198,10 +198,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // Full tiles: a uniform row base plus a fixed per-lane offset.  The last,
   // partial tile clamps every row to the last key (those rows are masked).
   const int ld_row = lane >> 4, ld_chunk = lane & 15;
-  uint32_t koff_ld[4];
+  // byte offsets from the tile's first key, the row of each load included, so
+  // that all loads of a tile share one scalar base (64 rows fit in 32 bits:
+  // the library limits heads so that 64 token rows span less than 2^31 bytes)
+  uint32_t koff_ld[4], voff_ld[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) koff_ld[i] = ld_row * rsb + 16 * (ld_chunk ^ (4 * i + ld_row));
-  const uint32_t voff_ld = ld_row * rsb + 16 * (ld_chunk ^ (4 * ld_row));
+  for (int i = 0; i < 4; ++i) {
+    const int krow = 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
+    const int vrow = 16 * wave + 4 * i;
+    koff_ld[i] = (krow + ld_row) * rsb + 16 * (ld_chunk ^ (4 * i + ld_row));
+    voff_ld[i] = (vrow + ld_row) * rsb + 16 * (ld_chunk ^ (4 * ld_row));
+  }
   // a tile known to hold kBN keys
   auto issue_full_tile = [&](auto S, int t) __attribute__((always_inline)) {
     const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
@@ -210,10 +217,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int blk = 4 * wave + i;
-      const int krow = 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
-      const int vrow = 16 * wave + 4 * i;
-      dma16(kt + (size_t)krow * rsb, koff_ld[i], st + blk * 1024);
-      dma16(vt + (size_t)vrow * rsb, voff_ld, st + kHalfTile + blk * 1024);
+      dma16(kt, koff_ld[i], st + blk * 1024);
+      dma16(vt, voff_ld[i], st + kHalfTile + blk * 1024);
     }
   };
   auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {

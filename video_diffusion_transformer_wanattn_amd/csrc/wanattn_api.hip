@@ -118,6 +118,8 @@ wanattn_status check_tensor_sizes(int32_t B, int32_t N, int32_t heads, int32_t h
   if (N > (1 << 30)) return fail(WANATTN_E_INVALID, "N=%d above 2^30 tokens", N);
   if (head_dim != kHeadDim) return fail(WANATTN_E_UNSUPPORTED, "head_dim %d (only 128 is built)", head_dim);
   if ((long long)B * N * heads * kHeadDim > (1ll << 40)) return fail(WANATTN_E_INVALID, "tensor too large");
+  // the attention kernels address 64 consecutive token rows with 32-bit offsets
+  if (heads > WANATTN_MAX_HEADS) return fail(WANATTN_E_UNSUPPORTED, "heads=%d above %d", heads, WANATTN_MAX_HEADS);
   return WANATTN_OK;
 }
 

@@ -221,6 +221,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       dma16(vt, voff_ld[i], st + kHalfTile + blk * 1024);
     }
   };
+  // load n (0..7) of a full tile: K (n even) or V (n odd) rows of group n / 2
+  auto issue_one = [&](auto S, int t, int n) __attribute__((always_inline)) {
+    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
+    const int i = n >> 1, blk = 4 * wave + i;
+    if (n & 1) dma16(vbase + (size_t)t * kBN * rsb, voff_ld[i], st + kHalfTile + blk * 1024);
+    else dma16(kbase + (size_t)t * kBN * rsb, koff_ld[i], st + blk * 1024);
+  };
   auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {
     const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
     const char* kt = kbase + (size_t)t * kBN * rsb;
@@ -487,10 +494,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
     const int j = 2 * t + kb;
     if constexpr (!decltype(MASKED)::value) {
+      // the loads of tile t+3 are spread over the QK^T groups below
       if (kb == 0) {
         wait_vm<8>();
         tile_barrier();
-        issue_full_tile(SNN, t + 3);
       }
     } else if (kb == 0 && t + 1 < nt) {
       if (t + 2 < nt) wait_vm<8>();
@@ -523,6 +530,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       // and would otherwise be sunk past it
       asm volatile("" : "+v"(pk1[kk >> 2][kk & 3]));
       if (kk < 6) load_vop(S, kb, 1 + kk / 2, kk & 1);
+      if constexpr (!decltype(MASKED)::value) {
+        if (kb == 0) issue_one(SNN, t + 3, kk);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 pb[2][2];

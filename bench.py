@@ -28,6 +28,39 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_wan14b_720p_81f_hbm_traffic.txt")
+
+
+def kernel_sources_digest():
+    """sha256 over the kernel sources, the public header and the build script
+    (the flags the library is compiled with live there)."""
+    import glob
+    import hashlib
+    pkg = os.path.join(ROOT, "video_diffusion_transformer_wanattn_amd")
+    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*")))
+    files += [os.path.join(ROOT, "include", "wanattn.h"), os.path.join(pkg, "build.py")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per self-attention launch from the committed counter summary,
+    or None when it was taken on other kernel sources or another workload."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_SUMMARY) if ":" in line)
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("source_sha256") != kernel_sources_digest() or fields.get("workload") != workload:
+        return None
+    try:
+        return int(fields["attn_fetch_bytes_per_launch"]) + int(fields["attn_write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -117,6 +150,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device copy of BYTES bytes after the timed "
+                         "region (a known-size kernel for calibrating memory counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -176,6 +212,16 @@ def main():
         step(per[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.copy_probe > 0:
+        # an elementwise kernel that reads BYTES and writes BYTES (a same-device
+        # copy_ may go to a DMA engine, which the shader counters do not see)
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe} bytes")
+        del src, dst
     self_ms = [e[0].elapsed_time(e[1]) for e in per]
     cross_ms = [e[1].elapsed_time(e[2]) for e in per]
     step_ms = wall * 1e3 / args.steps
@@ -208,7 +254,7 @@ def main():
                    "rope_theta": 10000.0, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_fwd_kernel (wanattn_self)",
+                     "traffic": measured_traffic(wl.name), "kernel": "attn_fwd_kernel (wanattn_self)",
                      "flops_per_launch": f_self},
         "self_ms": round(self_avg, 3),
         "self_ms_min": round(min(self_ms), 3),

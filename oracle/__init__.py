@@ -62,6 +62,9 @@ def _load():
                                       f64, f64, i32, i32, P, i32, P, P, i32]
         lib.orc_self_rows.restype = i32
         lib.orc_cross_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, P, i32, P, P, i32]
+        lib.orc_kv_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                    f64, f64, P, i32, P, P, i32]
+        lib.orc_kv_rows.restype = i32
         lib.orc_cross_rows.restype = i32
         lib.orc_token_grid.argtypes = [i32, i32, i32, P]
         lib.orc_token_grid.restype = None
@@ -146,6 +149,35 @@ def self_rows(q, k, v, grid, rows=None, theta: float = 10000.0, scale: float | N
                                rows.ctypes.data, out.ctypes.data, _threads(threads))
     if rc != 0:
         raise ValueError("orc_self_rows rejected its arguments")
+    return out
+
+
+def kv_rows(q, k, v, grid_q, kv_frame0: int = 0, rows=None, theta: float = 10000.0,
+            scale: float | None = None, kv_lens=None, threads: int | None = None):
+    """A chunk of queries against a key/value cache (Self Forcing streaming).
+
+    q: [B, Nq, heads, d] on the grid ``grid_q`` = (Fq, H, W, f0, h0, w0) (the
+    chunk's first frame is f0); k, v: [B, Nkv, heads, d], Nkv / (H W) whole
+    frames whose first frame is ``kv_frame0``, raw (the oracle rotates them).
+    Every key j < kv_lens[b] is visible.  Returns fp64 [B, len(rows), heads, d]."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Nq, heads, d = q.shape
+    Nkv = k.shape[1]
+    assert k.shape == (B, Nkv, heads, d) and v.shape == k.shape
+    Fq, H, W, f0, h0, w0 = grid_q
+    if rows is None:
+        rows = np.arange(Nq, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    kvl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
+    out = np.empty((B, rows.shape[0], heads, d), dtype=np.float64)
+    rc = _load().orc_kv_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Nq, Nkv, heads, d, Fq, H, W,
+                             int(f0), int(kv_frame0), int(h0), int(w0), theta, scale,
+                             None if kvl is None else kvl.ctypes.data, rows.shape[0], rows.ctypes.data,
+                             out.ctypes.data, _threads(threads))
+    if rc != 0:
+        raise ValueError("orc_kv_rows rejected its arguments")
     return out
 
 

@@ -35,6 +35,10 @@
  *    floor(f_i / C), C = chunk_frames latent frames per chunk, counted from
  *    frame 0 of the grid.
  *  - kv_len: keys j >= kv_len are excluded (all query rows still computed).
+ *  - KV-cache streaming: a chunk of queries (first frame f0) attends to every
+ *    cached key, earlier chunks and its own; the cache holds whole frames whose
+ *    positions are their own frame indices (first frame kv_frame0), so a
+ *    rolling window only moves positions.
  *
  * Parity pins for every function here live in tests/test_oracle_pins.py.
  */
@@ -156,7 +160,8 @@ typedef struct {
   /* shared */
   const uint16_t *q, *k, *v;
   int B, N, M, heads, head_dim;
-  int H, W, f0, h0, w0;
+  int H, W, f0, h0, w0;    /* grid and position offsets of the queries */
+  int kf0, kh0, kw0;       /* position offsets of the keys (same grid H x W) */
   double theta, scale;
   int rope, mask, chunk_frames;
   const int* kv_lens;
@@ -195,7 +200,7 @@ static void* run_task(void* arg) {
       if (t->rope) {
         int pos[3];
         orc_decode(j, t->H, t->W, pos);
-        orc_rope_vec(qtmp, kmat + (size_t)j * d, d, pos[0] + t->f0, pos[1] + t->h0, pos[2] + t->w0,
+        orc_rope_vec(qtmp, kmat + (size_t)j * d, d, pos[0] + t->kf0, pos[1] + t->kh0, pos[2] + t->kw0,
                      t->theta);
       } else {
         memcpy(kmat + (size_t)j * d, qtmp, sizeof(double) * d);
@@ -299,11 +304,65 @@ int orc_self_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B
   t.f0 = f0;
   t.h0 = h0;
   t.w0 = w0;
+  t.kf0 = f0;
+  t.kh0 = h0;
+  t.kw0 = w0;
   t.theta = theta;
   t.scale = scale;
   t.rope = 1;
   t.mask = mask;
   t.chunk_frames = chunk_frames;
+  t.kv_lens = kv_lens;
+  t.nrows = nrows;
+  t.rows = rows;
+  t.out = out;
+  return run_threads(&t, nthreads);
+}
+
+/*
+ * Attention of one chunk of queries to a key/value cache ([P3] "ルート3 · Self
+ * Forcing": a new chunk attends to the chunks generated before it and to
+ * itself; [P1] ch. 4 "3D RoPE" for the positions).  Queries q [B, Nq, heads,
+ * head_dim] form a frame-major Fq x H x W grid whose positions are shifted by
+ * (qf0, h0, w0); keys and values [B, Nkv, heads, head_dim] are Nkv / (H W)
+ * whole frames at positions shifted by (kf0, h0, w0).  Both are rotated here
+ * from the raw inputs; every key j < kv_lens[b] is visible.
+ * out: fp64 [B, nrows, heads, head_dim].
+ */
+int orc_kv_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int Nq, int Nkv,
+                int heads, int head_dim, int Fq, int H, int W, int qf0, int kf0, int h0, int w0,
+                double theta, double scale, const int* kv_lens, int nrows, const int* rows,
+                double* out, int nthreads) {
+  if (B < 1 || Nq < 1 || Nkv < 1 || heads < 1 || head_dim < 2 || (head_dim % 2)) return 1;
+  if (H < 1 || W < 1 || Nq != Fq * H * W || Nkv % (H * W)) return 1;
+  for (int r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= Nq) return 1;
+  if (kv_lens)
+    for (int b = 0; b < B; ++b)
+      if (kv_lens[b] < 1 || kv_lens[b] > Nkv) return 1;
+  task_t t;
+  memset(&t, 0, sizeof t);
+  t.q = q;
+  t.k = k;
+  t.v = v;
+  t.B = B;
+  t.N = Nq;
+  t.M = Nkv;
+  t.heads = heads;
+  t.head_dim = head_dim;
+  t.H = H;
+  t.W = W;
+  t.f0 = qf0;
+  t.h0 = h0;
+  t.w0 = w0;
+  t.kf0 = kf0;
+  t.kh0 = h0;
+  t.kw0 = w0;
+  t.theta = theta;
+  t.scale = scale;
+  t.rope = 1;
+  t.mask = 0;
+  t.chunk_frames = 1;
   t.kv_lens = kv_lens;
   t.nrows = nrows;
   t.rows = rows;

@@ -33,6 +33,8 @@ MUTANTS = {
     "cross_rotated": ("  t.rope = 0;\n", "  t.rope = 1;\n"),
     "bf16_widening": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
     "max_starts_at_zero": ("double m = -INFINITY;", "double m = 0.0;"),
+    "kv_keys_take_query_offset": ("pos[0] + t->kf0, pos[1] + t->kh0", "pos[0] + t->f0, pos[1] + t->kh0"),
+    "kv_query_offset_dropped": ("  t.f0 = qf0;\n", "  t.f0 = 0;\n"),
 }
 
 

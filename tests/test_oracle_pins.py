@@ -406,3 +406,84 @@ def test_oracle_rejects_bad_arguments():
         oracle.self_rows(q, q, q, (2, 3, 4), block_causal=True, chunk_frames=0)
     with pytest.raises(ValueError):
         oracle.cross_rows(q, q[:, :4], q[:, :4], ctx_lens=[5])
+
+
+# ---------------------------------------------------------------------------
+# KV-cache streaming ([P3] "ルート3 · Self Forcing": a new chunk attends to the
+# cached earlier chunks and to itself; [P1] ch. 4 "3D RoPE" for the positions)
+# ---------------------------------------------------------------------------
+
+def rotate_rows(x, F, H, W, off):
+    """numpy rotation of every token with explicit rotation matrices."""
+    pos = grid_positions(F, H, W, off)
+    xf = widen(x)
+    out = np.empty_like(xf)
+    for n, p in enumerate(pos):
+        R = rotation_matrix(p)
+        for b in range(x.shape[0]):
+            for h in range(x.shape[2]):
+                out[b, n, h] = R @ xf[b, n, h]
+    return out
+
+
+def test_kv_matches_explicit_rotations_and_library_sdpa():
+    Fq, Fk, H, W = 2, 5, 3, 4
+    f0, kf0, h0, w0 = 3, 0, 1, 2
+    q = bf16((2, Fq * H * W, 2, 128), 30, 1, 1.5)
+    k, v = (bf16((2, Fk * H * W, 2, 128), 30, s, 1.5) for s in (2, 3))
+    qr = rotate_rows(q, Fq, H, W, (f0, h0, w0))
+    kr = rotate_rows(k, Fk, H, W, (kf0, h0, w0))
+    got = oracle.kv_rows(q, k, v, (Fq, H, W, f0, h0, w0), kv_frame0=kf0)
+    np.testing.assert_allclose(got, sdpa(qr, kr, widen(v)), rtol=0, atol=1e-12)
+    kvl = [37, 60]
+    got = oracle.kv_rows(q, k, v, (Fq, H, W, f0, h0, w0), kv_frame0=kf0, kv_lens=kvl)
+    for b in range(2):
+        mask = np.zeros((Fq * H * W, Fk * H * W), dtype=bool)
+        mask[:, :kvl[b]] = True
+        want = sdpa(qr[b:b + 1], kr[b:b + 1], widen(v)[b:b + 1], mask)
+        np.testing.assert_allclose(got[b:b + 1], want, rtol=0, atol=1e-12)
+
+
+def test_kv_chunk_equals_block_causal_rows():
+    # chunk c of block-causal self attention over the whole clip is the chunk's
+    # queries (first frame c*C) against the cache of frames [0, (c+1) C)
+    F, H, W, C = 6, 3, 4, 2
+    HW = H * W
+    q, k, v = (bf16((1, F * HW, 2, 128), 31, s, 1.5) for s in (1, 2, 3))
+    full = oracle.self_rows(q, k, v, (F, H, W), block_causal=True, chunk_frames=C)
+    for c in range(F // C):
+        rows = slice(c * C * HW, (c + 1) * C * HW)
+        n = (c + 1) * C * HW
+        got = oracle.kv_rows(q[:, rows], k[:, :n], v[:, :n], (C, H, W, c * C, 0, 0), kv_frame0=0)
+        np.testing.assert_allclose(got, full[:, rows], rtol=0, atol=1e-12)
+
+
+def test_kv_rolling_window_depends_only_on_position_differences():
+    # a rolling cache window moves both the chunk and the cache frames alike
+    Fq, Fk, H, W = 1, 4, 2, 5
+    q = bf16((1, Fq * H * W, 2, 128), 32, 1, 1.5)
+    k, v = (bf16((1, Fk * H * W, 2, 128), 32, s, 1.5) for s in (2, 3))
+    a = oracle.kv_rows(q, k, v, (Fq, H, W, 4, 0, 0), kv_frame0=1)
+    b = oracle.kv_rows(q, k, v, (Fq, H, W, 9, 0, 0), kv_frame0=6)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    c = oracle.kv_rows(q, k, v, (Fq, H, W, 5, 0, 0), kv_frame0=1)
+    assert np.abs(a - c).max() > 1e-3           # a different relative position does change it
+
+
+def test_kv_single_visible_key_returns_its_value():
+    q = bf16((1, 6, 1, 128), 33, 1, 1.5)
+    k, v = (bf16((1, 18, 1, 128), 33, s, 1.5) for s in (2, 3))
+    got = oracle.kv_rows(q, k, v, (1, 2, 3, 2, 0, 0), kv_lens=[1])
+    np.testing.assert_allclose(got[0, :, 0], np.repeat(widen(v)[0, :1, 0], 6, axis=0), rtol=0, atol=1e-15)
+
+
+def test_kv_rejects_bad_arguments():
+    q = bf16((1, 12, 1, 128), 34, 1)
+    k = bf16((1, 30, 1, 128), 34, 2)
+    with pytest.raises(ValueError):
+        oracle.kv_rows(q, k[:, :28], k[:, :28], (2, 2, 3, 0, 0, 0))   # 28 keys are not whole 2x3 frames
+    oracle.kv_rows(q, k, k, (2, 2, 3, 0, 0, 0))                # 30 keys are 5 frames: accepted
+    with pytest.raises(ValueError):
+        oracle.kv_rows(q, k[:, :24], k[:, :24], (2, 2, 2, 0, 0, 0))   # Nq != Fq*H*W
+    with pytest.raises(ValueError):
+        oracle.kv_rows(q, k[:, :24], k[:, :24], (2, 2, 3, 0, 0, 0), kv_lens=[25])

@@ -141,6 +141,51 @@ def cpu_baseline(wl, t, threads):
     }
 
 
+def kv_stream_leg(torch, seeded, wa, steps, warmup):
+    """One streaming step of Self Forcing: rotate the new chunk's keys into the
+    cache (wanattn_rope3d) and attend the chunk's queries to the whole cache
+    (wanattn_self_kv).  Times both with HIP events on the launch stream."""
+    import numpy as np
+    wl = seeded.WORKLOADS["wan14b_480p_165f_causal"]
+    t = seeded.workload_tensors(wl, seed=0, cross=False)
+    hw = wl.H * wl.W
+    c0 = wl.F - wl.chunk_frames
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q = dev(t["q"][:, c0 * hw:])
+    k_raw, v = dev(t["k"]), dev(t["v"])
+    kc = wa.rope3d(k_raw, (wl.F, wl.H, wl.W))               # cache of the earlier chunks, rotated once
+    new_k = k_raw[:, c0 * hw:]
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        wa.rope3d(new_k, (wl.chunk_frames, wl.H, wl.W), offsets=(c0, 0, 0), out=kc[:, c0 * hw:])
+        if ev is not None:
+            ev[1].record(stream)
+        wa.self_attention_kv(q, kc, v, (wl.chunk_frames, wl.H, wl.W), offsets=(c0, 0, 0), out=o)
+        if ev is not None:
+            ev[2].record(stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    rope_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    nq, nkv = q.shape[1], k_raw.shape[1]
+    f = 4 * wl.head_dim * wl.heads * nq * nkv
+    log(f"kv stream: chunk {nq} x cache {nkv} x {wl.heads} heads: attention {attn_ms:.3f} ms, "
+        f"cache append {rope_ms:.3f} ms")
+    return {"workload": "wan14b_480p_165f_causal, last chunk (frames 39-41) against the 42-frame cache",
+            "q_tokens": nq, "kv_tokens": nkv, "heads": wl.heads, "flops": f,
+            "attn_ms": round(attn_ms, 4), "attn_tflops": round(f / (attn_ms * 1e-3) / 1e12, 2),
+            "attn_frac": round(f / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "append_rope_ms": round(rope_ms, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +195,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--kv-stream", action="store_true",
+                    help="also time one Self Forcing streaming step: the last 3-frame chunk of the "
+                         "165-frame, 40-head workload against its full 42-frame key/value cache")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes after the timed "
                          "region (a known-size kernel for calibrating memory counters)")
@@ -264,6 +312,8 @@ def main():
         "cross_gbs": round(cross_bytes / (cross_avg * 1e-3) / 1e9, 1),
         "cross_frac_hbm": round(cross_bytes / (cross_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
     }
+    if args.kv_stream:
+        result["kv_stream"] = kv_stream_leg(torch, seeded, wa, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
         result["cpu_baseline"] = cpu_baseline(wl, t, threads)

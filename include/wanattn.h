@@ -118,6 +118,23 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
 size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim);
 
 /*
+ * [P3] Self Forcing, streamed: one chunk of queries against a key/value cache
+ * of the chunks before it and itself ([P1] ch. 4 "3D RoPE" for positions).
+ * q, o: [B, Nq, heads, 128] with Nq = grid_q->F * H * W; grid_q's offsets are
+ *   the chunk's RoPE positions (f0 = the chunk's first latent frame).
+ * k_cache: [B, Nkv, heads, 128], keys ALREADY rotated by their own positions
+ *   (wanattn_rope3d with the cache's grid and offsets, once per appended
+ *   chunk); v_cache: [B, Nkv, heads, 128].  Nkv must be whole frames of
+ *   H x W tokens.  Every key j < kv_lens[b] is visible.
+ * kv_lens: HOST array [B] or NULL (= Nkv), 1 <= kv_lens[b] <= Nkv.
+ * o must not overlap the inputs.  No workspace; numerics as wanattn_self.
+ */
+wanattn_status wanattn_self_kv(const void* q, const void* k_cache, const void* v_cache, void* o,
+                               int32_t B, int32_t Nq, int32_t Nkv, int32_t heads, int32_t head_dim,
+                               const wanattn_grid3d* grid_q, double theta, float scale,
+                               const int32_t* kv_lens, void* stream);
+
+/*
  * [P2] cross attention, called as cross_attn(x, context, context_lens) in
  * [P1] ch. 4: o = softmax(q k_ctx^T * scale) v_ctx, no rotary embedding.
  * q, o: [B, N, heads, 128]; k_ctx, v_ctx: [B, M, heads, 128] (M text tokens,

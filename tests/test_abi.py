@@ -106,6 +106,28 @@ def test_self_rejects_bad_lengths(lib):
     assert call_self(lib, B=300, lens=big, ws_bytes=1 << 28) == wa.E_UNSUPPORTED
 
 
+def test_self_kv_rejects(lib):
+    # queries: 2 frames of 3x4 = 24 tokens; cache: 5 frames = 60 tokens
+    def call(q=A, k=B_, v=C, o=O, B=1, Nq=24, Nkv=60, heads=2, d=128, grid=None, theta=1e4,
+             scale=0.088, lens=None):
+        grid = grid if grid is not None else g(2, 3, 4, 3, 0, 0)
+        return lib.wanattn_self_kv(q, k, v, o, B, Nq, Nkv, heads, d, grid, theta, scale, lens, None)
+    assert call(k=None) == wa.E_INVALID
+    assert call(o=ctypes.c_void_p((4 << 30) + 8)) == wa.E_INVALID          # misaligned
+    assert call(Nq=25) == wa.E_INVALID                                      # Nq != F*H*W
+    assert call(Nkv=58) == wa.E_INVALID                                     # not whole frames
+    assert call(Nkv=0) == wa.E_INVALID
+    assert call(d=64) == wa.E_UNSUPPORTED
+    assert call(heads=65537) == wa.E_UNSUPPORTED
+    assert call(grid=g(2, 3, 4, 1023, 0, 0)) == wa.E_INVALID               # chunk positions past the table
+    assert call(theta=0.0) == wa.E_INVALID
+    assert call(scale=-1.0) == wa.E_INVALID
+    assert call(o=B_) == wa.E_INVALID                                       # o aliases the cache
+    assert call(lens=(ctypes.c_int32 * 1)(61)) == wa.E_INVALID
+    assert call(lens=(ctypes.c_int32 * 1)(0)) == wa.E_INVALID
+    assert lib.wanattn_last_error()
+
+
 def test_cross_rejects(lib):
     def call(q=A, k=B_, v=C, o=O, B=1, N=24, M=8, heads=2, d=128, scale=0.088, lens=None):
         return lib.wanattn_cross(q, k, v, o, B, N, M, heads, d, scale, lens, None)

@@ -295,6 +295,48 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
   return launch_attn<true, false>(p, B, kv_lens, (hipStream_t)stream);
 }
 
+wanattn_status wanattn_self_kv(const void* q, const void* k_cache, const void* v_cache, void* o,
+                               int32_t B, int32_t Nq, int32_t Nkv, int32_t heads, int32_t head_dim,
+                               const wanattn_grid3d* grid_q, double theta, float scale,
+                               const int32_t* kv_lens, void* stream) {
+  t_err[0] = 0;
+  if (!q || !k_cache || !v_cache || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, Nq, heads, head_dim));
+  WA_TRY(check_tensor_sizes(B, Nkv, heads, head_dim));
+  WA_TRY(check_grid(grid_q, Nq));
+  WA_TRY(check_theta(theta));
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
+  const long long hw = (long long)grid_q->H * grid_q->W;
+  if (Nkv % hw != 0) return fail(WANATTN_E_INVALID, "Nkv=%d is not whole frames of %lld tokens", Nkv, hw);
+  const size_t qbytes = (size_t)B * Nq * heads * kHeadDim * 2, kbytes = (size_t)B * Nkv * heads * kHeadDim * 2;
+  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k_cache, kbytes) || overlap(o, qbytes, v_cache, kbytes))
+    return fail(WANATTN_E_INVALID, "o overlaps an input");
+  WA_TRY(check_lens(B, kv_lens, Nkv, "kv_lens"));
+  AttnParams p;
+  memset(&p, 0, sizeof p);
+  const float2* tab = nullptr;
+  WA_TRY(table_for(theta, &tab));
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k_cache;
+  p.v = (const uint16_t*)v_cache;
+  p.o = (uint16_t*)o;
+  p.tab = tab;
+  p.N = Nq;
+  p.Nk = Nkv;
+  p.heads = heads;
+  p.qscale = scale * 1.4426950408889634f;
+  p.H = grid_q->H;
+  p.W = grid_q->W;
+  p.f0 = grid_q->f0;
+  p.h0 = grid_q->h0;
+  p.w0 = grid_q->w0;
+  p.inv_hw = 1.0 / ((double)grid_q->H * grid_q->W);
+  p.inv_w = 1.0 / (double)grid_q->W;
+  return launch_attn<true, false>(p, B, kv_lens, (hipStream_t)stream);
+}
+
 wanattn_status wanattn_cross(const void* q, const void* k_ctx, const void* v_ctx, void* o,
                              int32_t B, int32_t N, int32_t M, int32_t heads, int32_t head_dim,
                              float scale, const int32_t* ctx_lens, void* stream) {

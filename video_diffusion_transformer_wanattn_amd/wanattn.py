@@ -21,8 +21,9 @@ HEAD_DIM = 128
 MAX_POS = 1024
 MAX_LEN_BATCH = 256
 
-EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wanattn_cross",
-           "wanattn_prepare", "wanattn_status_string", "wanattn_last_error", "wanattn_version")
+EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wanattn_self_kv",
+           "wanattn_cross", "wanattn_prepare", "wanattn_status_string", "wanattn_last_error",
+           "wanattn_version")
 
 
 class WanattnError(RuntimeError):
@@ -57,6 +58,8 @@ def load_library(path: str = LIB_PATH):
     lib.wanattn_self.restype = ctypes.c_int
     lib.wanattn_self_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.wanattn_self_workspace_bytes.restype = ctypes.c_size_t
+    lib.wanattn_self_kv.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, G, f64, f32, P, P]
+    lib.wanattn_self_kv.restype = ctypes.c_int
     lib.wanattn_cross.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, P, P]
     lib.wanattn_cross.restype = ctypes.c_int
     lib.wanattn_prepare.argtypes = [f64]
@@ -166,6 +169,32 @@ def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = 
     _raise_on(lib.wanattn_self(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, heads, d, ctypes.byref(g),
                                float(theta), float(scale), mask, int(chunk_frames), lens,
                                _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def self_attention_kv(q, k_cache, v_cache, grid_q, theta: float = 10000.0, scale: float | None = None,
+                      kv_lens=None, offsets=(0, 0, 0), out=None, stream=None):
+    """One chunk of queries (grid_q frames at RoPE offsets ``offsets``) against a
+    key/value cache of whole frames; k_cache holds keys already rotated by
+    their own positions (see rope3d).  Every key j < kv_lens[b] is visible."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    B, Nq, heads, d = _dims(q, k_cache, v_cache, out)
+    Nkv = int(k_cache.shape[1])
+    if tuple(k_cache.shape) != (B, Nkv, heads, d) or tuple(v_cache.shape) != (B, Nkv, heads, d):
+        raise ValueError("k_cache and v_cache must be [B, Nkv, heads, head_dim] like q")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    if kv_lens is not None and len(kv_lens) != B:
+        raise ValueError("kv_lens needs one entry per batch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    g = _grid(grid_q, offsets)
+    _raise_on(lib.wanattn_self_kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Nq, Nkv, heads, d,
+                                  ctypes.byref(g), float(theta), float(scale), _lens(kv_lens, B),
+                                  _stream(stream)))
     return out
 
 

@@ -141,6 +141,44 @@ def cpu_baseline(wl, t, threads):
     }
 
 
+def cfg_leg(torch, wa, wl, q, k, v, kc, vc, steps, warmup):
+    """One classifier-free-guidance step: the conditional and unconditional
+    samples (the same latent tokens, two text contexts trimmed to 77 and 23
+    tokens) through self and cross attention in one launch each (B = 2)."""
+    grid = (wl.F, wl.H, wl.W)
+    q2, k2, v2 = (torch.cat([x, x]) for x in (q, k, v))
+    kc2 = torch.cat([kc, kc.flip(1)])
+    vc2 = torch.cat([vc, vc.flip(1)])
+    lens = [77, 23]
+    o2, oc2 = torch.empty_like(q2), torch.empty_like(q2)
+    stream = torch.cuda.current_stream()
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        wa.self_attention(q2, k2, v2, grid, out=o2)
+        if ev is not None:
+            ev[1].record(stream)
+        wa.cross_attention(q2, kc2, vc2, ctx_lens=lens, out=oc2)
+        if ev is not None:
+            ev[2].record(stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    s_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    c_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    f_self = 2 * 4 * wl.head_dim * wl.heads * wl.N * wl.N
+    f_cross = 4 * wl.head_dim * wl.heads * wl.N * sum(lens)
+    log(f"cfg pair: self {s_ms:.3f} ms, cross {c_ms:.3f} ms")
+    return {"batch": 2, "ctx_lens": lens, "self_ms": round(s_ms, 3), "cross_ms": round(c_ms, 4),
+            "self_tflops": round(f_self / (s_ms * 1e-3) / 1e12, 2),
+            "self_frac": round(f_self / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "cross_tflops_visible": round(f_cross / (c_ms * 1e-3) / 1e12, 2)}
+
+
 def kv_stream_leg(torch, seeded, wa, steps, warmup):
     """One streaming step of Self Forcing: rotate the new chunk's keys into the
     cache (wanattn_rope3d) and attend the chunk's queries to the whole cache
@@ -198,6 +236,9 @@ def main():
     ap.add_argument("--kv-stream", action="store_true",
                     help="also time one Self Forcing streaming step: the last 3-frame chunk of the "
                          "165-frame, 40-head workload against its full 42-frame key/value cache")
+    ap.add_argument("--cfg", action="store_true",
+                    help="also time one classifier-free-guidance step of the workload: both "
+                         "samples (same latent, text contexts of 77 and 23 tokens) in one launch")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes after the timed "
                          "region (a known-size kernel for calibrating memory counters)")
@@ -314,6 +355,9 @@ def main():
     }
     if args.kv_stream:
         result["kv_stream"] = kv_stream_leg(torch, seeded, wa, args.steps, args.warmup)
+    if args.cfg:
+        del o_self, o_cross
+        result["cfg_batch"] = cfg_leg(torch, wa, wl, q, k, v, kc, vc, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
         result["cpu_baseline"] = cpu_baseline(wl, t, threads)

@@ -65,6 +65,8 @@ def _load():
         lib.orc_kv_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                     f64, f64, P, i32, P, P, i32]
         lib.orc_kv_rows.restype = i32
+        lib.orc_prologue_rows.argtypes = [P] * 11 + [i32, i32, i32, f64, f64, i32, P, P, P, P, i32]
+        lib.orc_prologue_rows.restype = i32
         lib.orc_cross_rows.restype = i32
         lib.orc_token_grid.argtypes = [i32, i32, i32, P]
         lib.orc_token_grid.restype = None
@@ -179,6 +181,34 @@ def kv_rows(q, k, v, grid_q, kv_frame0: int = 0, rows=None, theta: float = 10000
     if rc != 0:
         raise ValueError("orc_kv_rows rejected its arguments")
     return out
+
+
+def prologue_rows(x, e0, e1, wq, bq, wk, bk, wv, bv, gq, gk, rows=None, eps_ln: float = 1e-6,
+                  eps_rms: float = 1e-6, threads: int | None = None):
+    """Self-attention prologue of one block: norm1(x) * (1 + e1) + e0, the q, k,
+    v projections, RMSNorm of q and k.  x bf16 bits [B, N, dim]; e0, e1 float32
+    [B, dim]; weights bf16 bits [dim, dim]; biases and gammas bf16 bits [dim].
+    Returns fp64 (q, k, v), each [B, len(rows), dim]."""
+    x = _u16(x)
+    B, N, dim = x.shape
+    ws = [_u16(w) for w in (wq, wk, wv)]
+    vs = [_u16(a) for a in (bq, bk, bv, gq, gk)]
+    assert all(w.shape == (dim, dim) for w in ws) and all(a.shape == (dim,) for a in vs)
+    e0 = np.ascontiguousarray(e0, dtype=np.float32).reshape(B, dim)
+    e1 = np.ascontiguousarray(e1, dtype=np.float32).reshape(B, dim)
+    if rows is None:
+        rows = np.arange(N, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    outs = [np.empty((B, rows.shape[0], dim), dtype=np.float64) for _ in range(3)]
+    rc = _load().orc_prologue_rows(x.ctypes.data, e0.ctypes.data, e1.ctypes.data, ws[0].ctypes.data,
+                                   vs[0].ctypes.data, ws[1].ctypes.data, vs[1].ctypes.data,
+                                   ws[2].ctypes.data, vs[2].ctypes.data, vs[3].ctypes.data,
+                                   vs[4].ctypes.data, B, N, dim, float(eps_ln), float(eps_rms),
+                                   rows.shape[0], rows.ctypes.data, outs[0].ctypes.data,
+                                   outs[1].ctypes.data, outs[2].ctypes.data, _threads(threads))
+    if rc != 0:
+        raise ValueError("orc_prologue_rows rejected its arguments")
+    return tuple(outs)
 
 
 def cross_rows(q, k_ctx, v_ctx, rows=None, scale: float | None = None, ctx_lens=None,

@@ -408,6 +408,127 @@ int orc_cross_rows(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, in
 }
 
 /*
+ * The self-attention prologue of one block ([P1] ch. 4, "1つの block の完全な
+ * forward" and "3D RoPE"): the input of self_attn is norm1(x) * (1 + e1) + e0
+ * with the modulation in fp32; inside it q, k, v are linear projections of
+ * that input, and q and k each pass an RMSNorm (QK-Norm) before RoPE.
+ * Readings (the pages do not print these layers): norm1 is a LayerNorm over
+ * dim without affine parameters, eps_ln inside the square root; the RMSNorm
+ * runs over the whole projection width dim with a learned weight (gamma),
+ * eps_rms inside the square root; projections are y W^T + b with W [dim, dim]
+ * (out, in) and b [dim].
+ * x: bf16 [B, N, dim]; e0, e1: fp32 [B, dim]; wq, wk, wv: bf16 [dim, dim];
+ * bq, bk, bv, gq, gk: bf16 [dim].  Outputs fp64 [B, nrows, dim] for the rows
+ * requested (q and k RMS-normalised, v as projected), before any rotation.
+ */
+static void linear_row(const double* y, const uint16_t* w, const uint16_t* b, int dim, double* out) {
+  for (int o = 0; o < dim; ++o) {
+    double acc = bf16_value(b[o]);
+    const uint16_t* wr = w + (size_t)o * dim;
+    for (int i = 0; i < dim; ++i) acc += y[i] * bf16_value(wr[i]);
+    out[o] = acc;
+  }
+}
+
+static void rms_norm_row(double* x, const uint16_t* g, int dim, double eps) {
+  double ss = 0.0;
+  for (int i = 0; i < dim; ++i) ss += x[i] * x[i];
+  const double inv = 1.0 / sqrt(ss / dim + eps);
+  for (int i = 0; i < dim; ++i) x[i] = x[i] * inv * bf16_value(g[i]);
+}
+
+typedef struct {
+  const uint16_t *x, *wq, *wk, *wv, *bq, *bk, *bv, *gq, *gk;
+  const float *e0, *e1;
+  int B, N, dim, nrows;
+  const int* rows;
+  double eps_ln, eps_rms;
+  double *oq, *ok, *ov;
+  int begin, end; /* flat (b, row) range */
+  int status;
+} pro_task_t;
+
+static void* run_pro_task(void* arg) {
+  pro_task_t* t = (pro_task_t*)arg;
+  const int dim = t->dim;
+  double* y = (double*)malloc(sizeof(double) * dim);
+  if (!y) {
+    t->status = 1;
+    return 0;
+  }
+  for (int br = t->begin; br < t->end; ++br) {
+    const int b = br / t->nrows, r = br % t->nrows;
+    const uint16_t* xr = t->x + ((size_t)b * t->N + t->rows[r]) * dim;
+    double mean = 0.0, var = 0.0;
+    for (int i = 0; i < dim; ++i) mean += bf16_value(xr[i]);
+    mean /= dim;
+    for (int i = 0; i < dim; ++i) {
+      const double d = bf16_value(xr[i]) - mean;
+      var += d * d;
+    }
+    var /= dim;
+    const double inv = 1.0 / sqrt(var + t->eps_ln);
+    for (int i = 0; i < dim; ++i)
+      y[i] = (bf16_value(xr[i]) - mean) * inv * (1.0 + (double)t->e1[(size_t)b * dim + i]) +
+             (double)t->e0[(size_t)b * dim + i];
+    const size_t off = ((size_t)b * t->nrows + r) * dim;
+    linear_row(y, t->wq, t->bq, dim, t->oq + off);
+    linear_row(y, t->wk, t->bk, dim, t->ok + off);
+    linear_row(y, t->wv, t->bv, dim, t->ov + off);
+    rms_norm_row(t->oq + off, t->gq, dim, t->eps_rms);
+    rms_norm_row(t->ok + off, t->gk, dim, t->eps_rms);
+  }
+  free(y);
+  return 0;
+}
+
+int orc_prologue_rows(const uint16_t* x, const float* e0, const float* e1, const uint16_t* wq,
+                      const uint16_t* bq, const uint16_t* wk, const uint16_t* bk, const uint16_t* wv,
+                      const uint16_t* bv, const uint16_t* gq, const uint16_t* gk, int B, int N, int dim,
+                      double eps_ln, double eps_rms, int nrows, const int* rows, double* oq, double* ok,
+                      double* ov, int nthreads) {
+  if (B < 1 || N < 1 || dim < 1 || nrows < 1 || !(eps_ln >= 0.0) || !(eps_rms >= 0.0)) return 1;
+  for (int r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= N) return 1;
+  const int total = B * nrows;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > total) nthreads = total;
+  if (nthreads > 256) nthreads = 256;
+  pro_task_t* tasks = (pro_task_t*)calloc((size_t)nthreads, sizeof(pro_task_t));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  int* started = (int*)calloc((size_t)nthreads, sizeof(int));
+  if (!tasks || !th || !started) {
+    free(tasks);
+    free(th);
+    free(started);
+    return 1;
+  }
+  for (int k = 0; k < nthreads; ++k) {
+    pro_task_t* t = &tasks[k];
+    t->x = x; t->wq = wq; t->wk = wk; t->wv = wv; t->bq = bq; t->bk = bk; t->bv = bv;
+    t->gq = gq; t->gk = gk; t->e0 = e0; t->e1 = e1;
+    t->B = B; t->N = N; t->dim = dim; t->nrows = nrows; t->rows = rows;
+    t->eps_ln = eps_ln; t->eps_rms = eps_rms; t->oq = oq; t->ok = ok; t->ov = ov;
+    t->begin = (int)((long)total * k / nthreads);
+    t->end = (int)((long)total * (k + 1) / nthreads);
+  }
+  for (int k = 1; k < nthreads; ++k) started[k] = pthread_create(&th[k], 0, run_pro_task, &tasks[k]) == 0;
+  run_pro_task(&tasks[0]);
+  int status = tasks[0].status;
+  for (int k = 1; k < nthreads; ++k) {
+    if (started[k])
+      pthread_join(th[k], 0);
+    else
+      run_pro_task(&tasks[k]);
+    status |= tasks[k].status;
+  }
+  free(tasks);
+  free(th);
+  free(started);
+  return status;
+}
+
+/*
  * [P1] ch. 2 "VAE" (vae_stride (4, 8, 8), the latent-shape expression and
  * "4n+1 の由来") and ch. 4 "latent から token へ" (patch (1, 2, 2)): a clip of
  * `frames` frames (4n+1) at height x width pixels becomes (frames-1)/4+1 latent frames of

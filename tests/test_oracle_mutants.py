@@ -35,6 +35,10 @@ MUTANTS = {
     "max_starts_at_zero": ("double m = -INFINITY;", "double m = 0.0;"),
     "kv_keys_take_query_offset": ("pos[0] + t->kf0, pos[1] + t->kh0", "pos[0] + t->f0, pos[1] + t->kh0"),
     "kv_query_offset_dropped": ("  t.f0 = qf0;\n", "  t.f0 = 0;\n"),
+    "ln_unbiased_variance": ("    var /= dim;\n", "    var /= (dim - 1);\n"),
+    "modulation_sign": ("* (1.0 + (double)t->e1", "* (1.0 - (double)t->e1"),
+    "rms_gamma_dropped": ("x[i] = x[i] * inv * bf16_value(g[i]);", "x[i] = x[i] * inv;"),
+    "projection_bias_dropped": ("double acc = bf16_value(b[o]);", "double acc = 0.0;"),
 }
 
 

@@ -487,3 +487,88 @@ def test_kv_rejects_bad_arguments():
         oracle.kv_rows(q, k[:, :24], k[:, :24], (2, 2, 2, 0, 0, 0))   # Nq != Fq*H*W
     with pytest.raises(ValueError):
         oracle.kv_rows(q, k[:, :24], k[:, :24], (2, 2, 3, 0, 0, 0), kv_lens=[25])
+
+
+# ---------------------------------------------------------------------------
+# self-attention prologue ([P1] ch. 4: norm1(x) * (1 + e1) + e0 in fp32, the
+# q/k/v projections, RMSNorm (QK-Norm) on q and k)
+# ---------------------------------------------------------------------------
+
+def prologue_inputs(B, N, dim, seed, eye=False, zero_w=False):
+    x = bf16((B, N, dim), seed, 1, 1.0)
+    w = [bf16((dim, dim), seed, 2 + i, 1.0 / math.sqrt(dim)) for i in range(3)]
+    if eye:
+        w = [seeded.f32_to_bf16_bits_array(np.eye(dim, dtype=np.float32)) for _ in range(3)]
+    if zero_w:
+        w = [np.zeros((dim, dim), dtype=np.uint16) for _ in range(3)]
+    b = [bf16((dim,), seed, 5 + i, 0.1) for i in range(3)]
+    g = [seeded.f32_to_bf16_bits_array((1.0 + widen(bf16((dim,), seed, 8 + i, 0.1))).astype(np.float32))
+         for i in range(2)]
+    rng = np.random.default_rng(seed)
+    e0 = rng.normal(0.0, 0.1, (B, dim)).astype(np.float32)
+    e1 = rng.normal(0.0, 0.1, (B, dim)).astype(np.float32)
+    return x, e0, e1, w, b, g
+
+
+def run_prologue(x, e0, e1, w, b, g, **kw):
+    return oracle.prologue_rows(x, e0, e1, w[0], b[0], w[1], b[1], w[2], b[2], g[0], g[1], **kw)
+
+
+def test_prologue_matches_library_layer_norm_linear_rms_norm():
+    F = torch.nn.functional
+    x, e0, e1, w, b, g = prologue_inputs(2, 7, 256, 50)
+    q, k, v = run_prologue(x, e0, e1, w, b, g, eps_ln=1e-6, eps_rms=1e-6)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    y = F.layer_norm(t(widen(x)), (256,), eps=1e-6) * (1 + t(e1.astype(np.float64))[:, None]) \
+        + t(e0.astype(np.float64))[:, None]
+    lin = [F.linear(y, t(widen(w[i])), t(widen(b[i]))) for i in range(3)]
+    want_q = F.rms_norm(lin[0], (256,), weight=t(widen(g[0])), eps=1e-6).numpy()
+    want_k = F.rms_norm(lin[1], (256,), weight=t(widen(g[1])), eps=1e-6).numpy()
+    np.testing.assert_allclose(q, want_q, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(k, want_k, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(v, lin[2].numpy(), rtol=0, atol=1e-10)
+
+
+def test_prologue_identity_projection_gives_the_normalised_row():
+    x, e0, e1, w, b, g = prologue_inputs(1, 5, 128, 51, eye=True)
+    zero = [np.zeros(128, dtype=np.uint16)] * 3
+    one = [seeded.f32_to_bf16_bits_array(np.ones(128, dtype=np.float32))] * 2
+    z = np.zeros((1, 128), dtype=np.float32)
+    q, k, v = run_prologue(x, z, z, w, zero, one, eps_ln=0.0, eps_rms=0.0)
+    xf = widen(x)
+    ln = (xf - xf.mean(-1, keepdims=True)) / xf.std(-1, keepdims=True)
+    np.testing.assert_allclose(v, ln, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(q, ln, rtol=0, atol=1e-12)     # unit rms already
+    # the modulation: v = LN(x) (1 + e1) + e0 exactly
+    _, _, v2 = run_prologue(x, e0[:1], e1[:1], w, zero, one, eps_ln=0.0, eps_rms=0.0)
+    np.testing.assert_allclose(v2, ln * (1 + e1[:1].astype(np.float64)) + e0[:1], rtol=0, atol=1e-12)
+
+
+def test_prologue_bias_only_and_invariances():
+    x, e0, e1, w, b, g = prologue_inputs(1, 6, 128, 52)
+    # no weights: v is the bias, q is the bias RMS-normalised times gamma
+    q, k, v = run_prologue(x, e0, e1, [np.zeros((128, 128), dtype=np.uint16)] * 3, b, g, eps_rms=0.0)
+    bf = [widen(a) for a in b]
+    np.testing.assert_allclose(v[0], np.tile(bf[2], (6, 1)), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(q[0, 0], bf[0] / np.sqrt(np.mean(bf[0] ** 2)) * widen(g[0]), rtol=0, atol=1e-12)
+    # LayerNorm ignores an exact rescaling of x; RMSNorm ignores one of W and b
+    base = run_prologue(x, e0, e1, w, b, g, eps_ln=0.0, eps_rms=0.0)
+    x4 = seeded.f32_to_bf16_bits_array((4.0 * widen(x)).astype(np.float32))
+    for a, c in zip(base, run_prologue(x4, e0, e1, w, b, g, eps_ln=0.0, eps_rms=0.0)):
+        np.testing.assert_allclose(a, c, rtol=0, atol=1e-12)
+    w2 = [seeded.f32_to_bf16_bits_array((2.0 * widen(a)).astype(np.float32)) for a in w]
+    b2 = [seeded.f32_to_bf16_bits_array((2.0 * widen(a)).astype(np.float32)) for a in b]
+    q2, k2, v2 = run_prologue(x, e0, e1, w2, b2, g, eps_ln=0.0, eps_rms=0.0)
+    np.testing.assert_allclose(q2, base[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k2, base[1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(v2, 2.0 * base[2], rtol=0, atol=1e-12)
+
+
+def test_prologue_rows_subset_and_rejects():
+    x, e0, e1, w, b, g = prologue_inputs(2, 9, 128, 53)
+    full = run_prologue(x, e0, e1, w, b, g)
+    part = run_prologue(x, e0, e1, w, b, g, rows=[8, 0, 3])
+    for a, c in zip(full, part):
+        np.testing.assert_array_equal(a[:, [8, 0, 3]], c)
+    with pytest.raises(ValueError):
+        run_prologue(x, e0, e1, w, b, g, rows=[9])

@@ -224,6 +224,46 @@ def kv_stream_leg(torch, seeded, wa, steps, warmup):
             "append_rope_ms": round(rope_ms, 4)}
 
 
+def prologue_leg(torch, seeded, wa, wl, steps, warmup):
+    """The block's self-attention prologue at the workload's token count and
+    dim = heads * 128 (5120 for the 14B model): modulated LayerNorm, the three
+    q/k/v projections with bias, RMSNorm of q and k, in one wanattn_prologue
+    call timed with HIP events on the launch stream."""
+    import numpy as np
+    dim = wl.heads * wl.head_dim
+    t = seeded.prologue_tensors(wl.batch, wl.N, dim, seed=1)
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    d = {k: dev(v) for k, v in t.items() if k not in ("e0", "e1")}
+    e0, e1 = (torch.from_numpy(t[k]).cuda() for k in ("e0", "e1"))
+    out = tuple(torch.empty_like(d["x"]) for _ in range(3))
+    ws = torch.empty(wa.prologue_workspace_bytes(wl.batch, wl.N, dim), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        wa.prologue(d["x"], e0, e1, d["wq"], d["bq"], d["wk"], d["bk"], d["wv"], d["bv"], d["gq"], d["gk"],
+                    out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    rows = wl.batch * wl.N
+    gemm_flops = 3 * 2 * rows * dim * dim
+    row_bytes = 2 * rows * dim * 2 + 4 * rows * dim * 2     # LayerNorm x -> y, RMSNorm q, k in place
+    floor_ms = gemm_flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3 + row_bytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    log(f"prologue: {rows} tokens x dim {dim}: {ms:.3f} ms (floor {floor_ms:.3f} ms)")
+    return {"workload": f"{wl.name} prologue: {rows} tokens x dim {dim}", "ms": round(ms, 3),
+            "gemm_flops": gemm_flops, "row_pass_bytes": row_bytes,
+            "tflops_over_gemm_flops": round(gemm_flops / (ms * 1e-3) / 1e12, 2),
+            "floor_ms": round(floor_ms, 3), "frac_of_floor": round(floor_ms / ms, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +279,9 @@ def main():
     ap.add_argument("--cfg", action="store_true",
                     help="also time one classifier-free-guidance step of the workload: both "
                          "samples (same latent, text contexts of 77 and 23 tokens) in one launch")
+    ap.add_argument("--prologue", action="store_true",
+                    help="also time the block's self-attention prologue (modulated LayerNorm, q/k/v "
+                         "projections, QK RMSNorm) at the workload's tokens and dim = heads * 128")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes after the timed "
                          "region (a known-size kernel for calibrating memory counters)")
@@ -358,6 +401,8 @@ def main():
     if args.cfg:
         del o_self, o_cross
         result["cfg_batch"] = cfg_leg(torch, wa, wl, q, k, v, kc, vc, args.steps, args.warmup)
+    if args.prologue:
+        result["prologue"] = prologue_leg(torch, seeded, wa, wl, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
         result["cpu_baseline"] = cpu_baseline(wl, t, threads)

@@ -147,6 +147,43 @@ wanattn_status wanattn_cross(const void* q, const void* k_ctx, const void* v_ctx
                              float scale, const int32_t* ctx_lens, void* stream);
 
 /*
+ * [P1] ch. 4, the block forward up to self_attn, and "3D RoPE" (QK-Norm):
+ *   y = LayerNorm(x) * (1 + e1[b]) + e0[b]      (LayerNorm without affine
+ *       parameters over dim: mean, mean squared deviation, eps_ln in the root)
+ *   q = RMSNorm(y Wq^T + bq) * gq,  k = RMSNorm(y Wk^T + bk) * gk,
+ *   v = y Wv^T + bv                 (RMSNorm over the whole dim, eps_rms)
+ * x: [B, N, dim] bf16.  e0, e1: [B, dim] fp32 (the shift and scale of the
+ * block's time modulation).  wq, wk, wv: [dim, dim] bf16, row o holding output
+ * o's weights over the input columns (the nn.Linear layout).  bq, bk, bv, gq,
+ * gk: [dim] bf16.  q, k, v: [B, N, dim] bf16, i.e. [B, N, heads, 128] when
+ * dim = heads * 128, not yet rotated: they are wanattn_self's inputs.
+ * dim: a multiple of 8 in [8, 8192].  eps_ln, eps_rms: finite, >= 0 (the
+ * model uses 1e-6 for both).
+ * Numerics: LayerNorm statistics and modulation in fp32, y rounded to bf16;
+ * the projections are bf16 GEMMs with fp32 accumulation (hipBLASLt, bias added
+ * in fp32 in the epilogue), rounded to bf16; RMSNorm in fp32 on those values,
+ * rounded to bf16.  Pointers 16-byte aligned; q, k, v must not overlap each
+ * other or any input.
+ * workspace: caller-owned device memory of at least
+ *   wanattn_prologue_workspace_bytes(B, N, dim) bytes, 256-byte aligned, not
+ *   overlapping any tensor; it holds y and the GEMM library's workspace.
+ *   Contents after the call are unspecified; concurrent calls need separate
+ *   workspaces.
+ * The first call on a device creates that device's hipBLASLt handle (which
+ * may allocate device memory and synchronise), and the first call for each
+ * new (dim, B * N) runs the library's algorithm query; later calls only enqueue.
+ */
+wanattn_status wanattn_prologue(const void* x, const float* e0, const float* e1, const void* wq,
+                                const void* bq, const void* wk, const void* bk, const void* wv,
+                                const void* bv, const void* gq, const void* gk, void* q, void* k,
+                                void* v, int32_t B, int32_t N, int32_t dim, float eps_ln,
+                                float eps_rms, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* bytes of workspace wanattn_prologue needs for these sizes (0 for invalid sizes) */
+size_t wanattn_prologue_workspace_bytes(int32_t B, int32_t N, int32_t dim);
+
+/*
  * Build and upload the rotary table for theta on the current device now
  * (a blocking copy).  Otherwise this happens at the first call that uses
  * theta on a device; call it before capturing such calls in a HIP graph.

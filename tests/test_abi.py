@@ -152,6 +152,60 @@ def test_rope3d_rejects(lib):
     assert call(grid=g(2, 3, 4, 0, 0, 1021)) == wa.E_INVALID
 
 
+GEMM_WS = 128 << 20  # hipBLASLt's share of the prologue workspace
+
+
+def test_prologue_workspace_size(lib):
+    assert lib.wanattn_prologue_workspace_bytes(1, 24, 256) == 24 * 256 * 2 + GEMM_WS
+    assert lib.wanattn_prologue_workspace_bytes(2, 5, 8) == 256 + GEMM_WS      # y rounded up to 256 bytes
+    assert lib.wanattn_prologue_workspace_bytes(1, 24, 12) == 0
+    assert lib.wanattn_prologue_workspace_bytes(1, 24, 8200) == 0
+    assert lib.wanattn_prologue_workspace_bytes(0, 24, 256) == 0
+    assert lib.wanattn_prologue_workspace_bytes(1 << 12, 1 << 13, 128) == 0   # more than 2^24 tokens
+
+
+def test_prologue_rejects(lib):
+    # 14 tensors at distinct, far-apart, 256-byte aligned dummy addresses
+    base = [ctypes.c_void_p((i + 1) << 32) for i in range(14)]
+    ws = ctypes.c_void_p(15 << 32)
+
+    def call(ptrs=None, B=1, N=24, dim=256, eps_ln=1e-6, eps_rms=1e-6, ws=ws, ws_bytes=None):
+        ptrs = list(base) if ptrs is None else ptrs
+        if ws_bytes is None:
+            ws_bytes = 24 * 256 * 2 + GEMM_WS
+        return lib.wanattn_prologue(*ptrs, B, N, dim, eps_ln, eps_rms, ws, ws_bytes, None)
+
+    for i in range(14):                          # every pointer checked for NULL and alignment
+        ptrs = list(base)
+        ptrs[i] = None
+        assert call(ptrs) == wa.E_INVALID, i
+        ptrs[i] = ctypes.c_void_p(((i + 1) << 32) + 8)
+        assert call(ptrs) == wa.E_INVALID, i
+    assert call(B=0) == wa.E_INVALID
+    assert call(N=0) == wa.E_INVALID
+    assert call(dim=12) == wa.E_INVALID
+    assert call(dim=0) == wa.E_INVALID
+    assert call(dim=8200) == wa.E_UNSUPPORTED
+    assert call(B=1 << 12, N=1 << 13, dim=128, ws_bytes=1 << 40) == wa.E_UNSUPPORTED
+    assert call(eps_ln=-1e-6) == wa.E_INVALID
+    assert call(eps_rms=float("nan")) == wa.E_INVALID
+    assert call(eps_ln=float("inf")) == wa.E_INVALID
+    ptrs = list(base)
+    ptrs[11] = base[0]                           # q aliases x
+    assert call(ptrs) == wa.E_INVALID
+    ptrs = list(base)
+    ptrs[13] = ctypes.c_void_p((12 << 32) + 4096)  # v overlaps k
+    assert call(ptrs) == wa.E_INVALID
+    ptrs = list(base)
+    ptrs[12] = ctypes.c_void_p((4 << 32) + 16)   # k inside the bytes of wq (256 x 256 bf16)
+    assert call(ptrs) == wa.E_INVALID
+    assert call(ws=None) == wa.E_INVALID
+    assert call(ws=ctypes.c_void_p((15 << 32) + 16)) == wa.E_INVALID        # workspace not 256-aligned
+    assert call(ws_bytes=24 * 256 * 2 + GEMM_WS - 1) == wa.E_INVALID
+    assert call(ws=ctypes.c_void_p((14 << 32) - (1 << 20))) == wa.E_INVALID  # workspace runs into v
+    assert lib.wanattn_last_error()
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(1, 24, 2, 128, dtype=torch.bfloat16)
@@ -159,3 +213,9 @@ def test_binding_refuses_host_tensors():
         wa.rope3d(x, (2, 3, 4), out=x)
     with pytest.raises(ValueError):
         wa.self_attention(x, x, x, (2, 3, 4), out=x)
+    y = torch.zeros(1, 24, 256, dtype=torch.bfloat16)
+    w = torch.zeros(256, 256, dtype=torch.bfloat16)
+    b = torch.zeros(256, dtype=torch.bfloat16)
+    e = torch.zeros(1, 256)
+    with pytest.raises(ValueError):
+        wa.prologue(y, e, e, w, b, w, b, w, b, b, b, out=(y, y, y))

@@ -1,0 +1,129 @@
+"""GPU parity of the self-attention prologue (Wan2.2 source reading
+(blog.leeguoo.com), ch. 4, the block forward up to self_attn, and "3D RoPE"
+for the QK-Norm): modulated LayerNorm, q/k/v projections with bias, RMSNorm of
+q and k, against the fp64 oracle.
+
+Gates.  The GPU rounds three times to bf16 (the modulated LayerNorm output y,
+the projections, the normalised q and k), each a relative error of at most
+2^-9, and the projections sum dim products of the rounded y in fp32.  The
+outputs have unit-order RMS, so the bars are the attention gates restated
+relative to the output scale: rms(err) / rms(ref) <= 1e-2 (G2) and, per
+element, |err| <= 2e-2 * max(1, |ref|) (G1's absolute bound, widened in
+proportion for the few outputs above 1 in magnitude, where one bf16 ulp alone
+is 2^-8 |ref|).  A dropped bias, a dropped gamma or a wrong modulation sign
+moves rel_rms to 0.1 or more.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import errors, from_dev, to_dev, widen
+from video_diffusion_transformer_wanattn_amd import seeded
+from video_diffusion_transformer_wanattn_amd import wanattn as wa
+
+pytestmark = pytest.mark.gpu
+REL_RMS = 1e-2
+ELEM = 2e-2
+
+
+def to_dev_inputs(t):
+    d = {k: to_dev(v) for k, v in t.items() if k not in ("e0", "e1")}
+    d["e0"] = torch.from_numpy(t["e0"]).to("cuda")
+    d["e1"] = torch.from_numpy(t["e1"]).to("cuda")
+    return d
+
+
+def gpu_prologue(d, eps_ln=1e-6, eps_rms=1e-6):
+    out = wa.prologue(d["x"], d["e0"], d["e1"], d["wq"], d["bq"], d["wk"], d["bk"], d["wv"], d["bv"],
+                      d["gq"], d["gk"], eps_ln=eps_ln, eps_rms=eps_rms)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_prologue(t, rows=None, eps_ln=1e-6, eps_rms=1e-6):
+    return oracle.prologue_rows(t["x"], t["e0"], t["e1"], t["wq"], t["bq"], t["wk"], t["bk"], t["wv"],
+                                t["bv"], t["gq"], t["gk"], rows=rows, eps_ln=eps_ln, eps_rms=eps_rms)
+
+
+def check(got_bits, ref, what):
+    e = errors(got_bits, ref)
+    d = np.abs(widen(got_bits) - ref)
+    worst = float(np.max(d / np.maximum(1.0, np.abs(ref))))
+    msg = f"{what}: {e}, worst scaled {worst:.3g}"
+    print(msg, flush=True)
+    assert e["finite"], msg
+    assert e["rel_rms"] <= REL_RMS, msg
+    assert worst <= ELEM, msg
+    return e
+
+
+@pytest.mark.parametrize("B,N,dim,shift", [(2, 37, 256, 0.0), (1, 300, 1536, 0.0), (2, 65, 640, 20.0)])
+def test_prologue_all_rows(B, N, dim, shift):
+    # ragged token counts (37, 300, 65 rows: partial 4-row blocks), dims that
+    # are whole (256, 1536 = Wan 1.3B) or partial (640) 512-column chunks, and
+    # a hidden state far from zero mean (shift 20) for the LayerNorm centring
+    t = seeded.prologue_tensors(B, N, dim, seed=60 + dim, x_shift=shift, x_sigma=4.0 if shift else 1.0)
+    q, k, v = gpu_prologue(to_dev_inputs(t))
+    rq, rk, rv = oracle_prologue(t)
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check(from_dev(got), ref, f"prologue {name} B={B} N={N} dim={dim} shift={shift}")
+
+
+def test_prologue_eps_and_smallest_dim():
+    # dim = 8 (one 16-byte chunk per row, most lanes idle); a larger eps is
+    # visible in the result
+    t = seeded.prologue_tensors(1, 9, 8, seed=70)
+    d = to_dev_inputs(t)
+    for eps in (1e-6, 0.5):
+        q, k, v = gpu_prologue(d, eps_ln=eps, eps_rms=eps)
+        rq, rk, rv = oracle_prologue(t, eps_ln=eps, eps_rms=eps)
+        for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+            check(from_dev(got), ref, f"prologue {name} dim=8 eps={eps}")
+
+
+def test_prologue_feeds_self_attention():
+    # the outputs viewed as [B, N, heads, 128] are the attention inputs
+    F, H, W, heads = 2, 3, 5, 2
+    t = seeded.prologue_tensors(1, F * H * W, heads * 128, seed=71)
+    q, k, v = gpu_prologue(to_dev_inputs(t))
+    shp = (1, F * H * W, heads, 128)
+    o = wa.self_attention(q.view(shp), k.view(shp), v.view(shp), (F, H, W))
+    torch.cuda.synchronize()
+    ref = oracle.self_rows(from_dev(q).reshape(shp), from_dev(k).reshape(shp), from_dev(v).reshape(shp),
+                           (F, H, W), theta=10000.0)
+    e = errors(from_dev(o), ref)
+    assert e["rel_rms"] <= REL_RMS, e
+
+
+def test_prologue_wan14b_720p_sampled_rows():
+    # the Wan 14B block at 720p, 81 frames: 75,600 tokens x dim 5120, as the
+    # benchmark times it; sampled rows against the oracle, and every row of q
+    # and k against the RMSNorm identity rms(q / gamma) = 1
+    N, dim = 21 * 45 * 80, 5120
+    t = seeded.prologue_tensors(1, N, dim, seed=72)
+    q, k, v = gpu_prologue(to_dev_inputs(t))
+    rows = seeded.sample_rows(N, 40, seed=72)
+    rq, rk, rv = oracle_prologue(t, rows=rows)
+    idx = torch.from_numpy(rows.astype(np.int64)).to("cuda")
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check(from_dev(got[:, idx]), ref, f"prologue {name} 75600x5120 sampled")
+    for name, got, g in (("q", q, t["gq"]), ("k", k, t["gk"])):
+        gam = torch.from_numpy(seeded.bf16_bits_to_f32(g)).to("cuda")
+        r = torch.sqrt(torch.mean((got.float() / gam) ** 2, dim=-1))
+        lo, hi = float(r.min()), float(r.max())
+        assert 0.99 <= lo and hi <= 1.01, (name, lo, hi)
+
+
+def test_prologue_errors():
+    t = seeded.prologue_tensors(1, 4, 16, seed=73)
+    d = to_dev_inputs(t)
+    with pytest.raises(ValueError):
+        wa.prologue(d["x"], d["e0"], d["e1"], d["wq"], d["bq"], d["wk"], d["bk"], d["wv"], d["bv"],
+                    d["gq"], d["gk"][:8])
+    x12 = torch.zeros(1, 4, 12, dtype=torch.bfloat16, device="cuda")
+    w12 = torch.zeros(12, 12, dtype=torch.bfloat16, device="cuda")
+    b12 = torch.zeros(12, dtype=torch.bfloat16, device="cuda")
+    e12 = torch.zeros(1, 12, device="cuda")
+    with pytest.raises(wa.WanattnError):
+        wa.prologue(x12, e12, e12, w12, b12, w12, b12, w12, b12, b12, b12)

@@ -45,7 +45,8 @@ def _run(cmd):
 
 def build_hip() -> str:
     tmp = LIB + ".tmp"
-    _run([HIPCC, *HIP_FLAGS, "-o", tmp, os.path.join(CSRC, "wanattn_api.hip")])
+    # the q/k/v projections of the prologue are plain GEMMs in hipBLASLt
+    _run([HIPCC, *HIP_FLAGS, "-o", tmp, os.path.join(CSRC, "wanattn_api.hip"), "-lhipblaslt"])
     os.replace(tmp, LIB)
     return LIB
 

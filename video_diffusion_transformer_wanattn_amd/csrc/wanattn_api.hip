@@ -2,6 +2,7 @@
 // The operations are defined in include/wanattn.h.
 
 #include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
 
 #include <cmath>
 #include <cstdarg>
@@ -10,6 +11,7 @@
 #include <mutex>
 
 #include "attn_fwd.h"
+#include "prologue.h"
 #include "rope3d.h"
 #include "wanattn.h"
 
@@ -201,6 +203,113 @@ wanattn_status rope3d_checked(const void* x, void* y, int32_t B, int32_t N, int3
   return launched("rope3d");
 }
 
+// ---- q/k/v projections: plain bf16 GEMMs in hipBLASLt ---------------------
+
+constexpr size_t kGemmWorkspace = size_t(128) << 20;  // hipBLASLt's share of the prologue workspace
+constexpr long long kMaxPrologueRows = 1ll << 24;    // B * N tokens per prologue call
+
+hipblasLtHandle_t g_lt[kMaxDevices];
+
+// algorithm chosen by the library's heuristic for one (device, dim, rows) shape
+struct GemmPlan {
+  int dev = -1, dim = 0;
+  long long rows = 0;
+  hipblasLtMatmulAlgo_t algo;
+  size_t ws = 0;
+};
+constexpr int kPlans = 32;
+GemmPlan g_plans[kPlans];
+int g_plan_next = 0;
+
+#define LT_TRY(call, what)                                                        \
+  do {                                                                            \
+    hipblasStatus_t s_ = (call);                                                  \
+    if (s_ != HIPBLAS_STATUS_SUCCESS)                                             \
+      return fail(WANATTN_E_HIP, "%s: hipBLASLt status %d", what, (int)s_);      \
+  } while (0)
+
+// descriptors of out[rows, dim] = y[rows, dim] W^T + bias, all row-major bf16.
+// In the library's column-major terms D = op(A) B with m = dim (output
+// features), n = rows (tokens), k = dim: A is W read as a k x m matrix and
+// transposed, B is y read as k x n, D is the output read as m x n, and the
+// bias (length m) is broadcast over the tokens.
+struct ProjDesc {
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, d = nullptr;
+  ~ProjDesc() {
+    if (d) hipblasLtMatrixLayoutDestroy(d);
+    if (b) hipblasLtMatrixLayoutDestroy(b);
+    if (a) hipblasLtMatrixLayoutDestroy(a);
+    if (op) hipblasLtMatmulDescDestroy(op);
+  }
+  wanattn_status init(int dim, long long rows) {
+    LT_TRY(hipblasLtMatmulDescCreate(&op, HIPBLAS_COMPUTE_32F, HIP_R_32F), "matmul descriptor");
+    const int32_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    const uint32_t epi = HIPBLASLT_EPILOGUE_BIAS;
+    const int32_t bias_type = HIP_R_16BF;
+    LT_TRY(hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof ta), "TRANSA");
+    LT_TRY(hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof tb), "TRANSB");
+    LT_TRY(hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof epi), "EPILOGUE");
+    LT_TRY(hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_type,
+                                           sizeof bias_type), "BIAS_DATA_TYPE");
+    LT_TRY(hipblasLtMatrixLayoutCreate(&a, HIP_R_16BF, dim, dim, dim), "layout A");
+    LT_TRY(hipblasLtMatrixLayoutCreate(&b, HIP_R_16BF, dim, rows, dim), "layout B");
+    LT_TRY(hipblasLtMatrixLayoutCreate(&d, HIP_R_16BF, dim, rows, dim), "layout D");
+    return WANATTN_OK;
+  }
+  wanattn_status set_bias(const void* bias) {
+    LT_TRY(hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof bias),
+           "BIAS_POINTER");
+    return WANATTN_OK;
+  }
+};
+
+// handle and algorithm for this shape on the current device (created on first use)
+wanattn_status gemm_plan(ProjDesc& pd, int dim, long long rows, hipblasLtHandle_t* h, GemmPlan* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(WANATTN_E_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(WANATTN_E_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_lt[dev]) LT_TRY(hipblasLtCreate(&g_lt[dev]), "hipblasLtCreate");
+  *h = g_lt[dev];
+  for (const GemmPlan& g : g_plans)
+    if (g.dev == dev && g.dim == dim && g.rows == rows) {
+      *out = g;
+      return WANATTN_OK;
+    }
+  hipblasLtMatmulPreference_t pref = nullptr;
+  LT_TRY(hipblasLtMatmulPreferenceCreate(&pref), "preference");
+  const uint64_t max_ws = kGemmWorkspace;
+  hipblasStatus_t s = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                            &max_ws, sizeof max_ws);
+  // the best-ranked candidate whose workspace fits (some library builds rank
+  // candidates above the workspace preference)
+  constexpr int kCand = 8;
+  hipblasLtMatmulHeuristicResult_t res[kCand];
+  int count = 0;
+  if (s == HIPBLAS_STATUS_SUCCESS)
+    s = hipblasLtMatmulAlgoGetHeuristic(*h, pd.op, pd.a, pd.b, pd.d, pd.d, pref, kCand, res, &count);
+  hipblasLtMatmulPreferenceDestroy(pref);
+  if (s != HIPBLAS_STATUS_SUCCESS) return fail(WANATTN_E_HIP, "algorithm query: hipBLASLt status %d", (int)s);
+  int pick = -1;
+  for (int i = 0; i < count && i < kCand && pick < 0; ++i)
+    if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= kGemmWorkspace) pick = i;
+  if (pick < 0)
+    return fail(WANATTN_E_UNSUPPORTED, "hipBLASLt has no algorithm for a %d x %d x %lld bf16 GEMM with bias "
+                "within %zu bytes of workspace", dim, dim, rows, kGemmWorkspace);
+  GemmPlan& g = g_plans[g_plan_next];
+  g_plan_next = (g_plan_next + 1) % kPlans;
+  g.dev = dev;
+  g.dim = dim;
+  g.rows = rows;
+  g.algo = res[pick].algo;
+  g.ws = res[pick].workspaceSize;
+  *out = g;
+  return WANATTN_OK;
+}
+
+size_t prologue_y_bytes(long long rows, int dim) { return ((size_t)rows * dim * 2 + 255) & ~size_t(255); }
+
 }  // namespace
 
 extern "C" {
@@ -367,6 +476,99 @@ wanattn_status wanattn_cross(const void* q, const void* k_ctx, const void* v_ctx
   p.inv_hw = 1.0;
   p.inv_w = 1.0;
   return launch_attn<false, false>(p, B, ctx_lens, (hipStream_t)stream);
+}
+
+size_t wanattn_prologue_workspace_bytes(int32_t B, int32_t N, int32_t dim) {
+  if (B < 1 || N < 1 || dim < 8 || dim > kMaxRowDim || dim % 8 != 0) return 0;
+  if ((long long)B * N > kMaxPrologueRows) return 0;
+  return prologue_y_bytes((long long)B * N, dim) + kGemmWorkspace;
+}
+
+wanattn_status wanattn_prologue(const void* x, const float* e0, const float* e1, const void* wq,
+                                const void* bq, const void* wk, const void* bk, const void* wv,
+                                const void* bv, const void* gq, const void* gk, void* q, void* k,
+                                void* v, int32_t B, int32_t N, int32_t dim, float eps_ln,
+                                float eps_rms, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  t_err[0] = 0;
+  const void* ins[11] = {x, e0, e1, wq, bq, wk, bk, wv, bv, gq, gk};
+  void* outs[3] = {q, k, v};
+  for (const void* a : ins)
+    if (!a) return fail(WANATTN_E_INVALID, "null input pointer");
+  for (const void* a : outs)
+    if (!a) return fail(WANATTN_E_INVALID, "null output pointer");
+  for (const void* a : ins)
+    if (!aligned16(a)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  for (const void* a : outs)
+    if (!aligned16(a)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  if (B < 1 || N < 1) return fail(WANATTN_E_INVALID, "B and N must be >= 1");
+  if (dim < 8 || dim % 8 != 0) return fail(WANATTN_E_INVALID, "dim=%d must be a positive multiple of 8", dim);
+  if (dim > kMaxRowDim) return fail(WANATTN_E_UNSUPPORTED, "dim=%d above %d", dim, kMaxRowDim);
+  const long long rows = (long long)B * N;
+  if (rows > kMaxPrologueRows) return fail(WANATTN_E_UNSUPPORTED, "B*N=%lld above %lld tokens", rows, kMaxPrologueRows);
+  if (!(eps_ln >= 0.0f) || !std::isfinite(eps_ln) || !(eps_rms >= 0.0f) || !std::isfinite(eps_rms))
+    return fail(WANATTN_E_INVALID, "eps_ln and eps_rms must be finite and >= 0");
+  const size_t act = (size_t)rows * dim * 2, mat = (size_t)dim * dim * 2, vec = (size_t)dim * 2,
+               mod = (size_t)B * dim * 4;
+  const size_t in_bytes[11] = {act, mod, mod, mat, vec, mat, vec, mat, vec, vec, vec};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 11; ++j)
+      if (overlap(outs[i], act, ins[j], in_bytes[j])) return fail(WANATTN_E_INVALID, "an output overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], act, outs[j], act)) return fail(WANATTN_E_INVALID, "q, k and v overlap");
+  }
+  if (!workspace) return fail(WANATTN_E_INVALID, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(WANATTN_E_INVALID, "workspace must be 256-byte aligned");
+  const size_t need = prologue_y_bytes(rows, dim) + kGemmWorkspace;
+  if (workspace_bytes < need)
+    return fail(WANATTN_E_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  for (int j = 0; j < 11; ++j)
+    if (overlap(workspace, need, ins[j], in_bytes[j])) return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
+  for (int i = 0; i < 3; ++i)
+    if (overlap(workspace, need, outs[i], act)) return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
+
+  ProjDesc pd;
+  WA_TRY(pd.init(dim, rows));
+  hipblasLtHandle_t h = nullptr;
+  GemmPlan plan;
+  WA_TRY(gemm_plan(pd, dim, rows, &h, &plan));
+  const hipStream_t st = (hipStream_t)stream;
+  uint16_t* y = (uint16_t*)workspace;
+  void* gemm_ws = (char*)workspace + prologue_y_bytes(rows, dim);
+
+  LnModParams lp;
+  lp.x = (const uint16_t*)x;
+  lp.e0 = e0;
+  lp.e1 = e1;
+  lp.y = y;
+  lp.rows = rows;
+  lp.N = N;
+  lp.dim = dim;
+  lp.eps = eps_ln;
+  hipError_t le = launch_rows<LnModLaunch>(dim, dim3((unsigned)((rows + 3) / 4)), st, lp);
+  if (le != hipSuccess) return fail(WANATTN_E_HIP, "ln_mod launch: %s", hipGetErrorString(le));
+
+  const float one = 1.0f, zero = 0.0f;
+  const void* w[3] = {wq, wk, wv};
+  const void* bias[3] = {bq, bk, bv};
+  for (int i = 0; i < 3; ++i) {
+    WA_TRY(pd.set_bias(bias[i]));
+    LT_TRY(hipblasLtMatmul(h, pd.op, &one, w[i], pd.a, y, pd.b, &zero, outs[i], pd.d, outs[i], pd.d, &plan.algo,
+                           gemm_ws, plan.ws, st),
+           "projection GEMM");
+  }
+
+  RmsParams rp;
+  rp.q = (uint16_t*)q;
+  rp.k = (uint16_t*)k;
+  rp.gq = (const uint16_t*)gq;
+  rp.gk = (const uint16_t*)gk;
+  rp.rows = rows;
+  rp.dim = dim;
+  rp.eps = eps_rms;
+  le = launch_rows<QkRmsLaunch>(dim, dim3((unsigned)((2 * rows + 3) / 4)), st, rp);
+  if (le != hipSuccess) return fail(WANATTN_E_HIP, "qk_rmsnorm launch: %s", hipGetErrorString(le));
+  return WANATTN_OK;
 }
 
 }  // extern "C"

@@ -145,6 +145,29 @@ def workload_tensors(wl: Workload, seed: int = 0, threads: int | None = None,
     return out
 
 
+PROLOGUE_STREAM = 1 << 20   # stream numbers of the prologue tensors start here
+
+
+def prologue_tensors(B: int, N: int, dim: int, seed: int = 0, x_sigma: float = 1.0,
+                     x_shift: float = 0.0, mod_sigma: float = 0.5, threads: int | None = None):
+    """Inputs of the self-attention prologue as bf16 bits (e0/e1 as float32):
+    x [B, N, dim] ~ N(x_shift, x_sigma^2); Wq, Wk, Wv [dim, dim] ~ N(0, 1/dim)
+    (nn.Linear layout); biases ~ N(0, 0.1^2); RMSNorm gammas 1 + N(0, 0.1^2);
+    the modulation shift e0 and scale e1 [B, dim] ~ N(0, mod_sigma^2)."""
+    st = PROLOGUE_STREAM
+    g = lambda shape, i, sig: normal_bf16(shape, seed, st + i, sig, threads)
+    x = g((B, N, dim), 0, x_sigma)
+    if x_shift:
+        x = f32_to_bf16_bits_array(bf16_bits_to_f32(x) + np.float32(x_shift))
+    w = [g((dim, dim), 1 + i, 1.0 / np.sqrt(dim)) for i in range(3)]
+    b = [g((dim,), 4 + i, 0.1) for i in range(3)]
+    gam = [f32_to_bf16_bits_array(np.float32(1.0) + bf16_bits_to_f32(g((dim,), 7 + i, 0.1))) for i in range(2)]
+    e0 = bf16_bits_to_f32(g((B, dim), 9, mod_sigma)).copy()
+    e1 = bf16_bits_to_f32(g((B, dim), 10, mod_sigma)).copy()
+    return {"x": x, "e0": e0, "e1": e1, "wq": w[0], "wk": w[1], "wv": w[2], "bq": b[0], "bk": b[1],
+            "bv": b[2], "gq": gam[0], "gk": gam[1]}
+
+
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
 

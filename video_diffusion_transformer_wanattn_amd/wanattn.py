@@ -22,8 +22,8 @@ MAX_POS = 1024
 MAX_LEN_BATCH = 256
 
 EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wanattn_self_kv",
-           "wanattn_cross", "wanattn_prepare", "wanattn_status_string", "wanattn_last_error",
-           "wanattn_version")
+           "wanattn_cross", "wanattn_prologue", "wanattn_prologue_workspace_bytes", "wanattn_prepare",
+           "wanattn_status_string", "wanattn_last_error", "wanattn_version")
 
 
 class WanattnError(RuntimeError):
@@ -62,6 +62,10 @@ def load_library(path: str = LIB_PATH):
     lib.wanattn_self_kv.restype = ctypes.c_int
     lib.wanattn_cross.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, P, P]
     lib.wanattn_cross.restype = ctypes.c_int
+    lib.wanattn_prologue.argtypes = [P] * 14 + [i32, i32, i32, f32, f32, P, ctypes.c_size_t, P]
+    lib.wanattn_prologue.restype = ctypes.c_int
+    lib.wanattn_prologue_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.wanattn_prologue_workspace_bytes.restype = ctypes.c_size_t
     lib.wanattn_prepare.argtypes = [f64]
     lib.wanattn_prepare.restype = ctypes.c_int
     lib.wanattn_status_string.argtypes = [ctypes.c_int]
@@ -219,6 +223,53 @@ def cross_attention(q, k_ctx, v_ctx, scale: float | None = None, ctx_lens=None, 
     _raise_on(lib.wanattn_cross(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(out), B, N, M, heads, d,
                                 float(scale), lens, _stream(stream)))
     return out
+
+
+def prologue_workspace_bytes(B: int, N: int, dim: int) -> int:
+    return int(load_library().wanattn_prologue_workspace_bytes(B, N, dim))
+
+
+def prologue(x, e0, e1, wq, bq, wk, bk, wv, bv, gq, gk, eps_ln: float = 1e-6, eps_rms: float = 1e-6,
+             out=None, workspace=None, stream=None):
+    """The block's self-attention inputs from its hidden state: LayerNorm(x)
+    modulated by (e0, e1), the q/k/v projections, RMSNorm of q and k.
+
+    x: [B, N, dim] bf16; e0, e1: [B, dim] float32; weights [dim, dim] bf16
+    (nn.Linear layout); biases and gammas [dim] bf16.  Returns (q, k, v), each
+    [B, N, dim] bf16 (view them as [B, N, dim // 128, 128] for the attention
+    calls).  out: optional (q, k, v) tensors; workspace: optional GPU tensor of
+    at least prologue_workspace_bytes(B, N, dim) bytes, 256-byte aligned."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, dim]")
+    B, N, dim = (int(a) for a in x.shape)
+    if out is None:
+        out = tuple(torch.empty_like(x) for _ in range(3))
+    mats, vecs = (wq, wk, wv), (bq, bk, bv, gq, gk)
+    for t in (x, *out, *mats, *vecs):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("x, weights, biases, gammas and outputs must be contiguous bf16 GPU tensors")
+    for t in (e0, e1):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("e0 and e1 must be contiguous float32 GPU tensors")
+        if tuple(t.shape) != (B, dim):
+            raise ValueError("e0 and e1 must be [B, dim]")
+    if any(tuple(t.shape) != (B, N, dim) for t in out):
+        raise ValueError("outputs must be [B, N, dim]")
+    if any(tuple(t.shape) != (dim, dim) for t in mats) or any(tuple(t.shape) != (dim,) for t in vecs):
+        raise ValueError("weights must be [dim, dim] and biases/gammas [dim]")
+    need = int(lib.wanattn_prologue_workspace_bytes(B, N, dim))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _raise_on(lib.wanattn_prologue(_ptr(x), _ptr(e0), _ptr(e1), _ptr(wq), _ptr(bq), _ptr(wk), _ptr(bk),
+                                   _ptr(wv), _ptr(bv), _ptr(gq), _ptr(gk), _ptr(out[0]), _ptr(out[1]),
+                                   _ptr(out[2]), B, N, dim, float(eps_ln), float(eps_rms),
+                                   _ptr(workspace), ws_bytes, _stream(stream)))
+    return tuple(out)
 
 
 def prepare(theta: float = 10000.0):

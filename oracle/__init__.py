@@ -61,6 +61,9 @@ def _load():
         lib.orc_self_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                       f64, f64, i32, i32, P, i32, P, P, i32]
         lib.orc_self_rows.restype = i32
+        lib.orc_self_rows_heads.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            P, f64, i32, i32, P, i32, P, P, i32]
+        lib.orc_self_rows_heads.restype = i32
         lib.orc_cross_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, P, i32, P, P, i32]
         lib.orc_kv_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                     f64, f64, P, i32, P, P, i32]
@@ -129,8 +132,10 @@ def rope3d(x, grid, theta: float = 10000.0, offsets=(0, 0, 0)):
 
 def self_rows(q, k, v, grid, rows=None, theta: float = 10000.0, scale: float | None = None,
               block_causal: bool = False, chunk_frames: int = 1, kv_lens=None,
-              offsets=(0, 0, 0), threads: int | None = None):
+              offsets=(0, 0, 0), threads: int | None = None, theta_per_head=None):
     """Self attention with 3D RoPE for query ``rows`` (all rows if None).
+    ``theta_per_head`` ([heads], optional): multi-head RoPE jitter, head h
+    rotating with its own base (``theta`` is then unused).
 
     Returns fp64 [B, len(rows), heads, d]."""
     q, k, v = _u16(q), _u16(k), _u16(v)
@@ -144,6 +149,18 @@ def self_rows(q, k, v, grid, rows=None, theta: float = 10000.0, scale: float | N
         scale = 1.0 / np.sqrt(d)
     kvl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
     out = np.empty((B, rows.shape[0], heads, d), dtype=np.float64)
+    if theta_per_head is not None:
+        th = np.ascontiguousarray(theta_per_head, dtype=np.float64)
+        if th.shape != (heads,):
+            raise ValueError("theta_per_head needs one value per head")
+        rc = _load().orc_self_rows_heads(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, N, heads, d, F, H,
+                                         W, int(offsets[0]), int(offsets[1]), int(offsets[2]), th.ctypes.data,
+                                         scale, 1 if block_causal else 0, int(chunk_frames),
+                                         None if kvl is None else kvl.ctypes.data, rows.shape[0],
+                                         rows.ctypes.data, out.ctypes.data, _threads(threads))
+        if rc != 0:
+            raise ValueError("orc_self_rows_heads rejected its arguments")
+        return out
     rc = _load().orc_self_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, N, heads, d, F, H, W,
                                int(offsets[0]), int(offsets[1]), int(offsets[2]), theta, scale,
                                1 if block_causal else 0, int(chunk_frames),

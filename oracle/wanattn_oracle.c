@@ -22,7 +22,9 @@
  *       softmax(Q K_text^T / sqrt(d_k)) V_text.
  *  [P3] long-video survey (atlascloud.ai), "ルート3 · Self Forcing": the
  *       bidirectional full attention is replaced by causal attention over
- *       chunks, earlier chunks acting as a KV cache.
+ *       chunks, earlier chunks acting as a KV cache; "ルート2 · LoL": a random
+ *       per-head perturbation of the RoPE phase (multi-head RoPE jitter),
+ *       applied without training.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *  - rope_params(L, D) builds, for positions p < L, the angles p * w_k with
@@ -35,6 +37,10 @@
  *    floor(f_i / C), C = chunk_frames latent frames per chunk, counted from
  *    frame 0 of the grid.
  *  - kv_len: keys j >= kv_len are excluded (all query rows still computed).
+ *  - multi-head RoPE jitter: a phase offset that does not depend on position
+ *    cancels in q.k (both sides turn by it), so the perturbation is taken to
+ *    act on the phase rate: head h rotates with its own base theta_h (drawn
+ *    by the caller, e.g. theta * (1 + eps_h)), every other step unchanged.
  *  - KV-cache streaming: a chunk of queries (first frame f0) attends to every
  *    cached key, earlier chunks and its own; the cache holds whole frames whose
  *    positions are their own frame indices (first frame kv_frame0), so a
@@ -163,6 +169,7 @@ typedef struct {
   int H, W, f0, h0, w0;    /* grid and position offsets of the queries */
   int kf0, kh0, kw0;       /* position offsets of the keys (same grid H x W) */
   double theta, scale;
+  const double* head_theta; /* [heads] per-head RoPE base, or NULL (= theta) */
   int rope, mask, chunk_frames;
   const int* kv_lens;
   int nrows;
@@ -190,6 +197,7 @@ static void* run_task(void* arg) {
   for (int bh = t->begin; bh < t->end; ++bh) {
     int b = bh / t->heads, hd = bh % t->heads;
     int kvl = t->kv_lens ? t->kv_lens[b] : nk;
+    const double th = t->head_theta ? t->head_theta[hd] : t->theta;
     /* keys and values of this (b, head), keys rotated when self attention */
     for (int j = 0; j < nk; ++j) {
       size_t off = (((size_t)b * nk + j) * t->heads + hd) * d;
@@ -200,8 +208,7 @@ static void* run_task(void* arg) {
       if (t->rope) {
         int pos[3];
         orc_decode(j, t->H, t->W, pos);
-        orc_rope_vec(qtmp, kmat + (size_t)j * d, d, pos[0] + t->kf0, pos[1] + t->kh0, pos[2] + t->kw0,
-                     t->theta);
+        orc_rope_vec(qtmp, kmat + (size_t)j * d, d, pos[0] + t->kf0, pos[1] + t->kh0, pos[2] + t->kw0, th);
       } else {
         memcpy(kmat + (size_t)j * d, qtmp, sizeof(double) * d);
       }
@@ -213,7 +220,7 @@ static void* run_task(void* arg) {
       if (t->rope) {
         int pos[3];
         orc_decode(i, t->H, t->W, pos);
-        orc_rope_vec(qtmp, qrow, d, pos[0] + t->f0, pos[1] + t->h0, pos[2] + t->w0, t->theta);
+        orc_rope_vec(qtmp, qrow, d, pos[0] + t->f0, pos[1] + t->h0, pos[2] + t->w0, th);
       } else {
         memcpy(qrow, qtmp, sizeof(double) * d);
       }
@@ -308,6 +315,55 @@ int orc_self_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B
   t.kh0 = h0;
   t.kw0 = w0;
   t.theta = theta;
+  t.scale = scale;
+  t.rope = 1;
+  t.mask = mask;
+  t.chunk_frames = chunk_frames;
+  t.kv_lens = kv_lens;
+  t.nrows = nrows;
+  t.rows = rows;
+  t.out = out;
+  return run_threads(&t, nthreads);
+}
+
+/*
+ * Self attention with multi-head RoPE jitter ([P3] "ルート2 · LoL"): as
+ * orc_self_rows, except that head h rotates q and k with its own base
+ * theta_heads[h] (each finite and > 0).
+ */
+int orc_self_rows_heads(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int N, int heads,
+                        int head_dim, int F, int H, int W, int f0, int h0, int w0,
+                        const double* theta_heads, double scale, int mask, int chunk_frames,
+                        const int* kv_lens, int nrows, const int* rows, double* out, int nthreads) {
+  if (!theta_heads || heads < 1) return 1;
+  for (int h = 0; h < heads; ++h)
+    if (!(theta_heads[h] > 0.0) || !isfinite(theta_heads[h])) return 1;
+  if (B < 1 || N < 1 || head_dim < 2 || (head_dim % 2) || N != F * H * W) return 1;
+  if (mask && chunk_frames < 1) return 1;
+  for (int r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= N) return 1;
+  if (kv_lens)
+    for (int b = 0; b < B; ++b)
+      if (kv_lens[b] < 1 || kv_lens[b] > N) return 1;
+  task_t t;
+  memset(&t, 0, sizeof t);
+  t.q = q;
+  t.k = k;
+  t.v = v;
+  t.B = B;
+  t.N = N;
+  t.M = N;
+  t.heads = heads;
+  t.head_dim = head_dim;
+  t.H = H;
+  t.W = W;
+  t.f0 = f0;
+  t.h0 = h0;
+  t.w0 = w0;
+  t.kf0 = f0;
+  t.kh0 = h0;
+  t.kw0 = w0;
+  t.head_theta = theta_heads;
   t.scale = scale;
   t.rope = 1;
   t.mask = mask;

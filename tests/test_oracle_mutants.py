@@ -39,6 +39,11 @@ MUTANTS = {
     "modulation_sign": ("* (1.0 + (double)t->e1", "* (1.0 - (double)t->e1"),
     "rms_gamma_dropped": ("x[i] = x[i] * inv * bf16_value(g[i]);", "x[i] = x[i] * inv;"),
     "projection_bias_dropped": ("double acc = bf16_value(b[o]);", "double acc = 0.0;"),
+    "jitter_head_off_by_one": ("t->head_theta ? t->head_theta[hd] : t->theta;",
+                               "t->head_theta ? t->head_theta[(hd + 1) % t->heads] : t->theta;"),
+    "jitter_ignored": ("t->head_theta ? t->head_theta[hd] : t->theta;",
+                       "t->head_theta ? t->head_theta[0] : t->theta;"),
+    "jitter_keys_unjittered": ("pos[1] + t->kh0, pos[2] + t->kw0, th);", "pos[1] + t->kh0, pos[2] + t->kw0, 1e4);"),
 }
 
 

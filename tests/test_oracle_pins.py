@@ -62,13 +62,15 @@ def grid_positions(F, H, W, off=(0, 0, 0)):
             for f, h, w in itertools.product(range(F), range(H), range(W))]
 
 
-def brute_self(q, k, v, grid, causal=False, chunk=1, kv_len=None, off=(0, 0, 0)):
-    """Full N x N fp64 attention with RoPE, straight from the definition."""
+def brute_self(q, k, v, grid, causal=False, chunk=1, kv_len=None, off=(0, 0, 0), thetas=None):
+    """Full N x N fp64 attention with RoPE, straight from the definition;
+    ``thetas`` gives each head its own RoPE base (multi-head jitter)."""
     F, H, W = grid
     B, N, heads, d = q.shape
     Qf, Kf, Vf = widen(q), widen(k), widen(v)
     pos = grid_positions(F, H, W, off)
-    mats = [rotation_matrix(p, d) for p in pos]
+    thetas = [THETA] * heads if thetas is None else list(thetas)
+    head_mats = [[rotation_matrix(p, d, th) for p in pos] for th in thetas]
     out = np.zeros((B, N, heads, d))
     frame = np.array([p[0] - off[0] for p in pos])
     allowed = np.ones((N, N), dtype=bool)
@@ -78,6 +80,7 @@ def brute_self(q, k, v, grid, causal=False, chunk=1, kv_len=None, off=(0, 0, 0))
         allowed &= (np.arange(N)[None, :] < kv_len)
     for b in range(B):
         for h in range(heads):
+            mats = head_mats[h]
             Qr = np.stack([mats[n] @ Qf[b, n, h] for n in range(N)])
             Kr = np.stack([mats[n] @ Kf[b, n, h] for n in range(N)])
             S = Qr @ Kr.T / math.sqrt(d)
@@ -572,3 +575,62 @@ def test_prologue_rows_subset_and_rejects():
         np.testing.assert_array_equal(a[:, [8, 0, 3]], c)
     with pytest.raises(ValueError):
         run_prologue(x, e0, e1, w, b, g, rows=[9])
+
+
+# ---------------------------------------------------------------------------
+# multi-head RoPE jitter ([P3] "ルート2 · LoL"): head h rotates with its own base
+# ---------------------------------------------------------------------------
+
+JITTER_THETAS = [10000.0, 500.0, 2.0e5]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_jitter_matches_bruteforce(causal):
+    grid = (3, 2, 4)
+    N = 24
+    q, k, v = (bf16((2, N, 3, 128), 80, s, 1.0) for s in (1, 2, 3))
+    got = oracle.self_rows(q, k, v, grid, theta_per_head=JITTER_THETAS, block_causal=causal,
+                           chunk_frames=2, kv_lens=[N, 17], offsets=(1, 0, 2))
+    want = np.stack([brute_self(q[b:b + 1], k[b:b + 1], v[b:b + 1], grid, causal=causal, chunk=2,
+                                kv_len=kl, off=(1, 0, 2), thetas=JITTER_THETAS)[0]
+                     for b, kl in enumerate([N, 17])])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("axis,pair", [(0, 5), (1, 3), (2, 20)])
+def test_jitter_score_closed_form(axis, pair):
+    # one non-zero key at position 0 and a query L steps away along one axis:
+    # the key's probability is e^s / (e^s + N - 1) with s = c * cos(L * w) / sqrt(128),
+    # w = theta_h^(-2 pair / D) -- solved for s and compared per head
+    widths = [44, 42, 42]
+    L = 7
+    grid = [1, 1, 1]
+    grid[axis] = L + 1
+    N = L + 1
+    heads = len(JITTER_THETAS)
+    c = 64.0
+    base = sum(widths[a] for a in range(axis))        # first element of the axis segment
+    e = base + 2 * pair                                 # real part of the pair
+    q = np.zeros((1, N, heads, 128), dtype=np.uint16)
+    k = np.zeros_like(q)
+    v = np.zeros_like(q)
+    one = seeded.f32_to_bf16_bits(1.0)
+    q[0, L, :, e] = one
+    k[0, 0, :, e] = seeded.f32_to_bf16_bits(c)
+    v[0, 0, :, 0] = one
+    o = oracle.self_rows(q, k, v, tuple(grid), rows=[L], theta_per_head=JITTER_THETAS)
+    for h, th in enumerate(JITTER_THETAS):
+        p = o[0, 0, h, 0]
+        s = math.log(p / (1.0 - p) * (N - 1))
+        want = c * math.cos(L * th ** (-2.0 * pair / widths[axis])) / math.sqrt(128)
+        assert abs(s - want) < 1e-9, (h, s, want)
+
+
+def test_jitter_common_theta_is_plain_rope_and_rejects():
+    grid = (2, 3, 2)
+    q, k, v = (bf16((1, 12, 2, 128), 81, s, 1.0) for s in (1, 2, 3))
+    np.testing.assert_array_equal(oracle.self_rows(q, k, v, grid, theta=777.0),
+                                  oracle.self_rows(q, k, v, grid, theta_per_head=[777.0, 777.0]))
+    for bad in ([1e4], [1e4, 0.0], [1e4, -5.0], [1e4, float("nan")], [1e4, float("inf")]):
+        with pytest.raises(ValueError):
+            oracle.self_rows(q, k, v, grid, theta_per_head=bad)

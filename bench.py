@@ -224,6 +224,37 @@ def kv_stream_leg(torch, seeded, wa, steps, warmup):
             "append_rope_ms": round(rope_ms, 4)}
 
 
+def jitter_leg(torch, seeded, wa, wl, q, k, v, steps, warmup):
+    """Self attention with multi-head RoPE jitter (each head its own RoPE base,
+    seeded theta (1 + eps_h)): per-head tables built on the device, the keys
+    rotated with them, the attention kernel reading its head's table."""
+    thetas = seeded.jitter_thetas(wl.heads, seed=0)
+    grid = (wl.F, wl.H, wl.W)
+    o = torch.empty_like(q)
+    ws = torch.empty(wa.self_jitter_workspace_bytes(wl.batch, wl.N, wl.heads), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        wa.self_attention(q, k, v, grid, block_causal=wl.block_causal, chunk_frames=wl.chunk_frames,
+                          theta_per_head=thetas, out=o, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    f_self, _ = flops(wl)
+    log(f"jitter: self attention with per-head RoPE bases {ms:.3f} ms")
+    return {"ms": round(ms, 3), "tflops": round(f_self / (ms * 1e-3) / 1e12, 2),
+            "frac": round(f_self / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "thetas": "10000 (1 + eps_h), eps_h ~ N(0, 0.1^2) seeded"}
+
+
 def prologue_leg(torch, seeded, wa, wl, steps, warmup):
     """The block's self-attention prologue at the workload's token count and
     dim = heads * 128 (5120 for the 14B model): modulated LayerNorm, the three
@@ -279,6 +310,8 @@ def main():
     ap.add_argument("--cfg", action="store_true",
                     help="also time one classifier-free-guidance step of the workload: both "
                          "samples (same latent, text contexts of 77 and 23 tokens) in one launch")
+    ap.add_argument("--jitter", action="store_true",
+                    help="also time self attention with multi-head RoPE jitter (per-head RoPE bases)")
     ap.add_argument("--prologue", action="store_true",
                     help="also time the block's self-attention prologue (modulated LayerNorm, q/k/v "
                          "projections, QK RMSNorm) at the workload's tokens and dim = heads * 128")
@@ -401,6 +434,8 @@ def main():
     if args.cfg:
         del o_self, o_cross
         result["cfg_batch"] = cfg_leg(torch, wa, wl, q, k, v, kc, vc, args.steps, args.warmup)
+    if args.jitter:
+        result["jitter"] = jitter_leg(torch, seeded, wa, wl, q, k, v, args.steps, args.warmup)
     if args.prologue:
         result["prologue"] = prologue_leg(torch, seeded, wa, wl, args.steps, args.warmup)
     if not args.no_cpu_baseline:

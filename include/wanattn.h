@@ -15,7 +15,8 @@
  *       (0h-n0.github.io), section on the text encoder -- cross attention
  *       softmax(Q K_text^T / sqrt(d_k)) V_text.
  *  [P3] long-video survey (atlascloud.ai), "ルート3 · Self Forcing" --
- *       bidirectional attention replaced by causal attention over chunks.
+ *       bidirectional attention replaced by causal attention over chunks;
+ *       "ルート2 · LoL" -- multi-head RoPE jitter against sink collapse.
  *
  * Common conventions
  *  - Tensors are caller-owned DEVICE memory on the device that owns `stream`,
@@ -116,6 +117,32 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
 
 /* bytes of workspace wanattn_self needs for these sizes (0 for invalid sizes) */
 size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim);
+
+#define WANATTN_MAX_JITTER_HEADS 256
+
+/*
+ * [P3] "ルート2 · LoL" multi-head RoPE jitter: wanattn_self where head h
+ * rotates q and k with its own base theta_per_head[h].  [P3] describes the
+ * jitter only as a random per-head perturbation of the RoPE phase, applied
+ * without training; a phase offset that does not grow with position cancels
+ * in q.k, so the perturbation is taken on the base (the caller draws the
+ * values, e.g. theta * (1 + eps_h)).  Equal values reproduce wanattn_self.
+ * theta_per_head: HOST array [heads], each finite and > 0; heads <=
+ *   WANATTN_MAX_JITTER_HEADS (else WANATTN_E_UNSUPPORTED).
+ * workspace: at least wanattn_self_jitter_workspace_bytes(...) bytes, 16-byte
+ *   aligned, not overlapping q, k, v or o.  It receives the per-head rotary
+ *   tables (built on the device in fp64 and rounded to fp32 on every call,
+ *   768 KiB per head) followed by the rotated keys.  Everything else, including
+ *   errors and numerics, is as wanattn_self.
+ */
+wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, void* o, int32_t B,
+                                   int32_t N, int32_t heads, int32_t head_dim,
+                                   const wanattn_grid3d* grid, const double* theta_per_head, float scale,
+                                   wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* bytes of workspace wanattn_self_jitter needs (0 for invalid sizes) */
+size_t wanattn_self_jitter_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim);
 
 /*
  * [P3] Self Forcing, streamed: one chunk of queries against a key/value cache

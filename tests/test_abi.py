@@ -152,6 +152,35 @@ def test_rope3d_rejects(lib):
     assert call(grid=g(2, 3, 4, 0, 0, 1021)) == wa.E_INVALID
 
 
+def test_self_jitter_workspace_and_rejects(lib):
+    tab = 3 * 1024 * 32 * 8                       # one head's rotary table
+    assert lib.wanattn_self_jitter_workspace_bytes(2, 24, 3, 128) == 3 * tab + 2 * 24 * 3 * 128 * 2
+    assert lib.wanattn_self_jitter_workspace_bytes(1, 24, 257, 128) == 0
+    assert lib.wanattn_self_jitter_workspace_bytes(1, 24, 3, 64) == 0
+    th3 = (ctypes.c_double * 3)(1e4, 5e2, 2e5)
+    need = 3 * tab + 24 * 3 * 128 * 2
+
+    def call(q=A, k=B_, v=C, o=O, B=1, N=24, heads=3, d=128, grid=None, th=th3, scale=0.088, mask=0,
+             chunk=1, lens=None, ws=WS, ws_bytes=need):
+        return lib.wanattn_self_jitter(q, k, v, o, B, N, heads, d, grid if grid is not None else g(2, 3, 4),
+                                       th, scale, mask, chunk, lens, ws, ws_bytes, None)
+    assert call(th=None) == wa.E_INVALID
+    assert call(th=(ctypes.c_double * 3)(1e4, 0.0, 1e4)) == wa.E_INVALID
+    assert call(th=(ctypes.c_double * 3)(1e4, float("nan"), 1e4)) == wa.E_INVALID
+    assert call(th=(ctypes.c_double * 3)(1e4, 1e4, -1.0)) == wa.E_INVALID
+    assert call(heads=257, th=(ctypes.c_double * 257)(*([1e4] * 257))) == wa.E_UNSUPPORTED
+    assert call(d=64) == wa.E_UNSUPPORTED
+    assert call(N=23) == wa.E_INVALID
+    assert call(ws_bytes=need - 1) == wa.E_INVALID          # the tables count too
+    assert call(ws=None) == wa.E_INVALID
+    assert call(ws=ctypes.c_void_p((4 << 30) - 16)) == wa.E_INVALID  # workspace runs into o
+    assert call(o=B_) == wa.E_INVALID
+    assert call(mask=1, chunk=0) == wa.E_INVALID
+    assert call(scale=0.0) == wa.E_INVALID
+    assert call(lens=(ctypes.c_int32 * 1)(25)) == wa.E_INVALID
+    assert lib.wanattn_last_error()
+
+
 GEMM_WS = 128 << 20  # hipBLASLt's share of the prologue workspace
 
 

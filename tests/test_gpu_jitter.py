@@ -1,0 +1,77 @@
+"""GPU parity of multi-head RoPE jitter (long-video survey (atlascloud.ai),
+"ルート2 · LoL"; read as head h rotating q and k with its own RoPE base
+theta_h) against the fp64 oracle, with the attention gates G1 and G2 of
+parity_util.  The per-head rotary tables are built on the GPU in fp64 on every
+call; with equal bases the call must agree with the shared-table path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import assert_parity, errors, from_dev, to_dev
+from video_diffusion_transformer_wanattn_amd import seeded
+from video_diffusion_transformer_wanattn_amd import wanattn as wa
+
+pytestmark = pytest.mark.gpu
+
+
+def gen(shape, seed, stream, sigma):
+    return seeded.normal_bf16(shape, seed, stream, sigma)
+
+
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, [105, 61])])
+def test_jitter_all_rows(causal, lens):
+    # 3 x 5 x 7 = 105 tokens (ragged against the 64-key and 256-query tiles),
+    # three heads with bases far apart, peaked scores (sigma 1.5), offsets
+    grid, B, heads = (3, 5, 7), 2, 3
+    thetas = [10000.0, 500.0, 2.0e5]
+    q, k = (gen((B, 105, heads, 128), 90, s, 1.5) for s in (1, 2))
+    v = gen((B, 105, heads, 128), 90, 3, 0.5)
+    o = wa.self_attention(to_dev(q), to_dev(k), to_dev(v), grid, theta_per_head=thetas, block_causal=causal,
+                          chunk_frames=1, kv_lens=lens, offsets=(2, 1, 0))
+    torch.cuda.synchronize()
+    ref = oracle.self_rows(q, k, v, grid, theta_per_head=thetas, block_causal=causal, chunk_frames=1,
+                           kv_lens=lens, offsets=(2, 1, 0))
+    assert_parity(from_dev(o), ref, what=f"jitter causal={causal}")
+
+
+def test_jitter_equal_bases_match_shared_table_and_jitter_matters():
+    grid, heads = (4, 6, 5), 4
+    q, k = (gen((1, 120, heads, 128), 91, s, 1.5) for s in (1, 2))
+    v = gen((1, 120, heads, 128), 91, 3, 0.5)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    plain = from_dev(wa.self_attention(dq, dk, dv, grid, theta=777.0))
+    same = from_dev(wa.self_attention(dq, dk, dv, grid, theta_per_head=[777.0] * heads))
+    torch.cuda.synchronize()
+    e = errors(same, seeded.bf16_bits_to_f32(plain).astype(np.float64))
+    print(f"equal bases vs shared table: {e}, bitwise equal {np.mean(same == plain):.4f}", flush=True)
+    assert e["rel_rms"] <= 1e-3, e
+    jit = from_dev(wa.self_attention(dq, dk, dv, grid, theta_per_head=[777.0, 777.0, 60.0, 777.0]))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(jit[:, :, [0, 1, 3]], same[:, :, [0, 1, 3]])   # heads are independent
+    moved = errors(jit[:, :, 2], seeded.bf16_bits_to_f32(same[:, :, 2]).astype(np.float64))
+    assert moved["rel_rms"] > 0.05, moved
+
+
+def test_jitter_wan14b_720p_sampled_rows():
+    # the 75,600-token, 40-head workload with seeded per-head bases
+    # theta (1 + eps_h), eps_h ~ N(0, 0.1^2), as the benchmark times it
+    wl = seeded.WORKLOADS["wan14b_720p_81f"]
+    t = seeded.workload_tensors(wl, seed=0, cross=False)
+    thetas = seeded.jitter_thetas(wl.heads, seed=0)
+    grid = (wl.F, wl.H, wl.W)
+    o = wa.self_attention(to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"]), grid, theta_per_head=thetas)
+    torch.cuda.synchronize()
+    rows = seeded.sample_rows(wl.N, 24, seed=5)
+    got = from_dev(o)[:, rows]
+    ref = oracle.self_rows(t["q"], t["k"], t["v"], grid, rows=rows, theta_per_head=thetas)
+    assert_parity(got, ref, what="jitter 75600x40 sampled")
+
+
+def test_jitter_errors():
+    q = torch.zeros(1, 24, 2, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        wa.self_attention(q, q.clone(), q.clone(), (2, 3, 4), theta_per_head=[1e4])
+    with pytest.raises(wa.WanattnError):
+        wa.self_attention(q, q.clone(), q.clone(), (2, 3, 4), theta_per_head=[1e4, -1.0])

@@ -71,6 +71,7 @@ struct AttnParams {
   const uint16_t* v;
   uint16_t* o;
   const float2* tab;  // rotary table for the query (self attention only)
+  long long tab_hstride;  // float2 entries between consecutive heads' tables (0: one shared table)
   int N;              // query tokens per batch
   int Nk;             // key tokens per batch
   int heads;
@@ -267,6 +268,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // operand of K Q^T: lane holds d = 16 kk + 8 hh + 0..7 of its query.
   bf16x8 qf[2][8];
   int lim[2];
+  const float2* qtab = p.tab + (size_t)head * p.tab_hstride;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int i = i0 + wave * 64 + qb * 32 + r;
@@ -288,7 +290,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       u32x4 pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        pk[e] = rotate_pair<ROPE>(raw[e], p.tab, 8 * kk + 4 * hh + e, pf, ph, pw, p.qscale);
+        pk[e] = rotate_pair<ROPE>(raw[e], qtab, 8 * kk + 4 * hh + e, pf, ph, pw, p.qscale);
       qf[qb][kk] = __builtin_bit_cast(bf16x8, pk);
       // keep Q in AGPRs: the MFMA reads its B operand from there directly and
       // the arch VGPRs stay free for the scores and the softmax

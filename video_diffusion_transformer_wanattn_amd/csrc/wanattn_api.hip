@@ -169,24 +169,16 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
   return WANATTN_OK;
 }
 
-// 3D RoPE of a whole tensor on `stream` (checked arguments)
-wanattn_status rope3d_checked(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
-                              int32_t head_dim, const wanattn_grid3d* grid, double theta,
-                              hipStream_t stream) {
-  t_err[0] = 0;
-  if (!x || !y) return fail(WANATTN_E_INVALID, "null tensor pointer");
-  if (!aligned16(x) || !aligned16(y)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
-  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
-  WA_TRY(check_grid(grid, N));
-  WA_TRY(check_theta(theta));
-  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
-  if (x != y && overlap(x, bytes, y, bytes)) return fail(WANATTN_E_INVALID, "y partially overlaps x");
-  const float2* tab = nullptr;
-  WA_TRY(table_for(theta, &tab));
+// 3D RoPE of a whole tensor with the table(s) at `tab` (head h's table at
+// tab + h * hstride); arguments already checked
+wanattn_status rope3d_launch(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
+                             const wanattn_grid3d* grid, const float2* tab, long long hstride,
+                             hipStream_t stream) {
   RopeParams p;
   p.x = (const u32x4*)x;
   p.y = (u32x4*)y;
   p.tab = tab;
+  p.tab_hstride = hstride;
   p.chunks = (long long)B * N * heads * 16;
   p.N = N;
   p.heads = heads;
@@ -202,6 +194,88 @@ wanattn_status rope3d_checked(const void* x, void* y, int32_t B, int32_t N, int3
   hipLaunchKernelGGL(rope3d_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return launched("rope3d");
 }
+
+// 3D RoPE of a whole tensor on `stream` (checked arguments)
+wanattn_status rope3d_checked(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
+                              int32_t head_dim, const wanattn_grid3d* grid, double theta,
+                              hipStream_t stream) {
+  t_err[0] = 0;
+  if (!x || !y) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(y)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  WA_TRY(check_grid(grid, N));
+  WA_TRY(check_theta(theta));
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  if (x != y && overlap(x, bytes, y, bytes)) return fail(WANATTN_E_INVALID, "y partially overlaps x");
+  const float2* tab = nullptr;
+  WA_TRY(table_for(theta, &tab));
+  return rope3d_launch(x, y, B, N, heads, grid, tab, 0, stream);
+}
+
+// argument checks shared by the self-attention entry points (theta checked by
+// the caller); the workspace must hold ws_need bytes
+wanattn_status check_self(const void* q, const void* k, const void* v, const void* o, int32_t B, int32_t N,
+                          int32_t heads, int32_t head_dim, const wanattn_grid3d* grid, float scale,
+                          wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                          const void* workspace, size_t workspace_bytes, size_t ws_need) {
+  if (!q || !k || !v || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  WA_TRY(check_grid(grid, N));
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
+  if (mask != WANATTN_MASK_NONE && mask != WANATTN_MASK_BLOCK_CAUSAL)
+    return fail(WANATTN_E_INVALID, "unknown mask %d", (int)mask);
+  if (mask == WANATTN_MASK_BLOCK_CAUSAL && chunk_frames < 1)
+    return fail(WANATTN_E_INVALID, "chunk_frames must be >= 1 for the block-causal mask");
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
+    return fail(WANATTN_E_INVALID, "o overlaps an input");
+  if (!workspace) return fail(WANATTN_E_INVALID, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(WANATTN_E_INVALID, "workspace must be 16-byte aligned");
+  if (workspace_bytes < ws_need)
+    return fail(WANATTN_E_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, ws_need);
+  if (overlap(workspace, ws_need, q, bytes) || overlap(workspace, ws_need, k, bytes) ||
+      overlap(workspace, ws_need, v, bytes) || overlap(workspace, ws_need, o, bytes))
+    return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
+  return check_lens(B, kv_lens, N, "kv_lens");
+}
+
+// keys rotated once into kprime (with head h's table at tab + h * hstride);
+// the queries are rotated by the attention kernel as it loads them
+wanattn_status self_launch(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t N,
+                           int32_t heads, const wanattn_grid3d* grid, float scale, wanattn_mask mask,
+                           int32_t chunk_frames, const int32_t* kv_lens, void* kprime, const float2* tab,
+                           long long hstride, hipStream_t stream) {
+  WA_TRY(rope3d_launch(k, kprime, B, N, heads, grid, tab, hstride, stream));
+  AttnParams p;
+  memset(&p, 0, sizeof p);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)kprime;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.tab = tab;
+  p.tab_hstride = hstride;
+  p.N = N;
+  p.Nk = N;
+  p.heads = heads;
+  p.qscale = scale * 1.4426950408889634f;
+  p.H = grid->H;
+  p.W = grid->W;
+  p.f0 = grid->f0;
+  p.h0 = grid->h0;
+  p.w0 = grid->w0;
+  p.inv_hw = 1.0 / ((double)grid->H * grid->W);
+  p.inv_w = 1.0 / (double)grid->W;
+  if (mask == WANATTN_MASK_BLOCK_CAUSAL) {
+    long long ct = (long long)chunk_frames * grid->H * grid->W;
+    p.chunk_tokens = (int)(ct < N ? ct : N);
+    return launch_attn<true, true>(p, B, kv_lens, stream);
+  }
+  return launch_attn<true, false>(p, B, kv_lens, stream);
+}
+
+size_t jitter_table_bytes(int heads) { return (size_t)heads * kTabEntries * sizeof(float2); }
 
 // ---- q/k/v projections: plain bf16 GEMMs in hipBLASLt ---------------------
 
@@ -351,57 +425,50 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
                             wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
                             void* workspace, size_t workspace_bytes, void* stream) {
   t_err[0] = 0;
-  if (!q || !k || !v || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
-  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
-  WA_TRY(check_grid(grid, N));
   WA_TRY(check_theta(theta));
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
-  if (mask != WANATTN_MASK_NONE && mask != WANATTN_MASK_BLOCK_CAUSAL)
-    return fail(WANATTN_E_INVALID, "unknown mask %d", (int)mask);
-  if (mask == WANATTN_MASK_BLOCK_CAUSAL && chunk_frames < 1)
-    return fail(WANATTN_E_INVALID, "chunk_frames must be >= 1 for the block-causal mask");
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
-  if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
-    return fail(WANATTN_E_INVALID, "o overlaps an input");
-  if (!workspace) return fail(WANATTN_E_INVALID, "workspace is NULL");
-  if (!aligned16(workspace)) return fail(WANATTN_E_INVALID, "workspace must be 16-byte aligned");
-  if (workspace_bytes < bytes)
-    return fail(WANATTN_E_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, bytes);
-  if (overlap(workspace, bytes, q, bytes) || overlap(workspace, bytes, k, bytes) ||
-      overlap(workspace, bytes, v, bytes) || overlap(workspace, bytes, o, bytes))
-    return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
-  WA_TRY(check_lens(B, kv_lens, N, "kv_lens"));
-  AttnParams p;
-  memset(&p, 0, sizeof p);
+  WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
+                    workspace_bytes, bytes));
   const float2* tab = nullptr;
   WA_TRY(table_for(theta, &tab));
-  // keys rotated once into the workspace; the queries are rotated as the
-  // attention kernel loads them
-  WA_TRY(rope3d_checked(k, workspace, B, N, heads, head_dim, grid, theta, (hipStream_t)stream));
-  p.q = (const uint16_t*)q;
-  p.k = (const uint16_t*)workspace;
-  p.v = (const uint16_t*)v;
-  p.o = (uint16_t*)o;
-  p.tab = tab;
-  p.N = N;
-  p.Nk = N;
-  p.heads = heads;
-  p.qscale = scale * 1.4426950408889634f;
-  p.H = grid->H;
-  p.W = grid->W;
-  p.f0 = grid->f0;
-  p.h0 = grid->h0;
-  p.w0 = grid->w0;
-  p.inv_hw = 1.0 / ((double)grid->H * grid->W);
-  p.inv_w = 1.0 / (double)grid->W;
-  if (mask == WANATTN_MASK_BLOCK_CAUSAL) {
-    long long ct = (long long)chunk_frames * grid->H * grid->W;
-    p.chunk_tokens = (int)(ct < N ? ct : N);
-    return launch_attn<true, true>(p, B, kv_lens, (hipStream_t)stream);
-  }
-  return launch_attn<true, false>(p, B, kv_lens, (hipStream_t)stream);
+  return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens, workspace, tab, 0,
+                     (hipStream_t)stream);
+}
+
+size_t wanattn_self_jitter_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim) {
+  if (B < 1 || N < 1 || heads < 1 || heads > kMaxJitterHeads || head_dim != kHeadDim) return 0;
+  return jitter_table_bytes(heads) + (size_t)B * N * heads * kHeadDim * 2;
+}
+
+wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, void* o, int32_t B,
+                                   int32_t N, int32_t heads, int32_t head_dim,
+                                   const wanattn_grid3d* grid, const double* theta_per_head, float scale,
+                                   wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  t_err[0] = 0;
+  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  if (heads > kMaxJitterHeads)
+    return fail(WANATTN_E_UNSUPPORTED, "heads=%d above %d for per-head tables", heads, kMaxJitterHeads);
+  if (!theta_per_head) return fail(WANATTN_E_INVALID, "theta_per_head is NULL");
+  for (int h = 0; h < heads; ++h)
+    if (!(theta_per_head[h] > 0.0) || !std::isfinite(theta_per_head[h]))
+      return fail(WANATTN_E_INVALID, "theta_per_head[%d] must be finite and > 0", h);
+  const size_t tbytes = jitter_table_bytes(heads);
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
+                    workspace_bytes, tbytes + bytes));
+  TableParams tp;
+  memset(&tp, 0, sizeof tp);
+  tp.tab = (float2*)workspace;
+  tp.heads = heads;
+  for (int h = 0; h < heads; ++h) tp.theta[h] = theta_per_head[h];
+  const long long total = (long long)heads * kTabEntries;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, tp);
+  WA_TRY(launched("rope_table"));
+  return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens,
+                     (char*)workspace + tbytes, (const float2*)workspace, kTabEntries, (hipStream_t)stream);
 }
 
 wanattn_status wanattn_self_kv(const void* q, const void* k_cache, const void* v_cache, void* o,

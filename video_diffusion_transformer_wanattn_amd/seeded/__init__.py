@@ -168,6 +168,16 @@ def prologue_tensors(B: int, N: int, dim: int, seed: int = 0, x_sigma: float = 1
             "bv": b[2], "gq": gam[0], "gk": gam[1]}
 
 
+JITTER_STREAM = (1 << 20) + 64   # stream of the per-head RoPE base draws
+
+
+def jitter_thetas(heads: int, seed: int = 0, theta: float = 10000.0, sigma: float = 0.1) -> np.ndarray:
+    """Per-head RoPE bases theta * (1 + eps_h), eps_h ~ N(0, sigma^2) rounded to
+    bf16 (the random draws of multi-head RoPE jitter, passed to both sides)."""
+    eps = bf16_bits_to_f32(normal_bf16((heads,), seed, JITTER_STREAM, sigma)).astype(np.float64)
+    return theta * (1.0 + eps)
+
+
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
 

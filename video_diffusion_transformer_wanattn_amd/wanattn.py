@@ -20,8 +20,10 @@ MASK_NONE, MASK_BLOCK_CAUSAL = 0, 1
 HEAD_DIM = 128
 MAX_POS = 1024
 MAX_LEN_BATCH = 256
+MAX_JITTER_HEADS = 256
 
-EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wanattn_self_kv",
+EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wanattn_self_jitter",
+           "wanattn_self_jitter_workspace_bytes", "wanattn_self_kv",
            "wanattn_cross", "wanattn_prologue", "wanattn_prologue_workspace_bytes", "wanattn_prepare",
            "wanattn_status_string", "wanattn_last_error", "wanattn_version")
 
@@ -58,6 +60,11 @@ def load_library(path: str = LIB_PATH):
     lib.wanattn_self.restype = ctypes.c_int
     lib.wanattn_self_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.wanattn_self_workspace_bytes.restype = ctypes.c_size_t
+    lib.wanattn_self_jitter.argtypes = [P, P, P, P, i32, i32, i32, i32, G, P, f32, ctypes.c_int, i32, P,
+                                        P, ctypes.c_size_t, P]
+    lib.wanattn_self_jitter.restype = ctypes.c_int
+    lib.wanattn_self_jitter_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.wanattn_self_jitter_workspace_bytes.restype = ctypes.c_size_t
     lib.wanattn_self_kv.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, G, f64, f32, P, P]
     lib.wanattn_self_kv.restype = ctypes.c_int
     lib.wanattn_cross.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, P, P]
@@ -143,13 +150,20 @@ def self_workspace_bytes(B: int, N: int, heads: int, head_dim: int = HEAD_DIM) -
     return int(load_library().wanattn_self_workspace_bytes(B, N, heads, head_dim))
 
 
+def self_jitter_workspace_bytes(B: int, N: int, heads: int, head_dim: int = HEAD_DIM) -> int:
+    return int(load_library().wanattn_self_jitter_workspace_bytes(B, N, heads, head_dim))
+
+
 def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = None,
                    block_causal: bool = False, chunk_frames: int = 3, kv_lens=None,
-                   offsets=(0, 0, 0), out=None, workspace=None, stream=None):
+                   offsets=(0, 0, 0), out=None, workspace=None, stream=None, theta_per_head=None):
     """softmax(RoPE(q) RoPE(k)^T * scale) v, bidirectional or latent-frame block-causal.
 
-    workspace: optional GPU tensor of at least self_workspace_bytes(...) bytes
-    (the rotated keys go there); allocated per call when not given."""
+    theta_per_head: optional [heads] RoPE bases (multi-head RoPE jitter; theta
+    is then unused).  workspace: optional GPU tensor of at least
+    self_workspace_bytes(...) bytes (self_jitter_workspace_bytes(...) with
+    theta_per_head); the rotated keys (and per-head tables) go there; allocated
+    per call when not given."""
     import torch
     lib = load_library()
     if out is None:
@@ -164,12 +178,25 @@ def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = 
     g = _grid(grid, offsets)
     mask = MASK_BLOCK_CAUSAL if block_causal else MASK_NONE
     lens = _lens(kv_lens, B)
-    need = int(lib.wanattn_self_workspace_bytes(B, N, heads, d))
+    jitter = theta_per_head is not None
+    if jitter:
+        th = [float(x) for x in theta_per_head]
+        if len(th) != heads:
+            raise ValueError("theta_per_head needs one value per head")
+        th_arr = (ctypes.c_double * heads)(*th)
+        need = int(lib.wanattn_self_jitter_workspace_bytes(B, N, heads, d))
+    else:
+        need = int(lib.wanattn_self_workspace_bytes(B, N, heads, d))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
+    if jitter:
+        _raise_on(lib.wanattn_self_jitter(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, heads, d,
+                                          ctypes.byref(g), th_arr, float(scale), mask, int(chunk_frames),
+                                          lens, _ptr(workspace), ws_bytes, _stream(stream)))
+        return out
     _raise_on(lib.wanattn_self(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, heads, d, ctypes.byref(g),
                                float(theta), float(scale), mask, int(chunk_frames), lens,
                                _ptr(workspace), ws_bytes, _stream(stream)))

@@ -386,7 +386,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   auto exp_pair = [&](int qb, int sl, int e, u32x4& pk, float (&acc2)[2]) __attribute__((always_inline)) {
     const float p0 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e]);
     const float p1 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1]);
-    acc2[e & 1] += p0 + p1;
+    // pairs e = 0, 1 start the two partial sums (every caller takes e in
+    // order 0..3): assigning rather than adding to 0 saves an add, which the
+    // compiler may not drop itself (0 + x is not x for x = -0)
+    if (e < 2) acc2[e & 1] = p0 + p1;
+    else acc2[e & 1] += p0 + p1;
     pk[e] = pack_bf16x2(p0, p1);
   };
   // (half sl of the block: keys 16 sl .. 16 sl + 15, registers 8 sl .. 8 sl + 7)

@@ -305,6 +305,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[qb][db][j] = 0.0f;
+  // The O products (phase B below) are inline asm so that their accumulators
+  // live in AGPRs for the whole loop: the arch VGPRs then hold the scores,
+  // the operands and the loop invariants without parking any of them in AGPRs
+  // (which cost ~20 copies per block).  The compiler does not know these asm
+  // statements are MFMAs and inserts no wait states around them, so this fence
+  // does: 24 wait states (more than the 8-pass MFMA's result latency) before
+  // any VALU access of O after an O product, and after VALU writes of O
+  // (initialisation, rescale) before the next product reads them.  Dependent
+  // MFMA -> MFMA accumulation needs none (the hardware interlocks it).
+  auto acc_fence = [&]() __attribute__((always_inline)) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                   "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
+  };
+  acc_fence();
   // Running softmax reference per query row, kept as a bias b = -m added to the
   // scores inside the QK^T product: one extra MFMA k-step multiplies the K-side
   // constant (1, 1) with the Q-side (hi, lo), the bias split into two bf16
@@ -439,6 +454,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // again, and the scores of block j+1 (already formed against the old
   // reference) are shifted alike.  One wave-uniform branch for both row blocks.
   auto move_reference = [&](bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
+    acc_fence();
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float m = row_max(qb);
@@ -458,6 +474,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
       }
       softmax_exp_row(qb, pb, bsum);
     }
+    acc_fence();
+    // P was just rewritten by VALU and is read next by the O products
+    asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
   };
 
   // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored and
@@ -560,8 +579,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int db = g >> 1, sl = g & 1;
-      acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[0][sl], acc[0][db], 0, 0, 0);
-      acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][sl], pb[1][sl], acc[1][db], 0, 0, 0);
+      // O^T += V^T P^T with the accumulator in AGPRs (see acc_fence)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[0][db]) : "a"(vop[db][sl]), "v"(pb[0][sl]));
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[1][db]) : "a"(vop[db][sl]), "v"(pb[1][sl]));
       load_kop(SN, kb, g);
       if (g == 0) {
         take_scores();
@@ -607,6 +627,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   for (; t < nt; ++t) tile_step(t, t + 1, t + 3, Mask{}, t);
 
   // ---- epilogue: O = O^T / l, bf16; lane holds d = 32 db + 8 g4 + 4 hh + 0..3
+  acc_fence();
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float inv = 1.0f / wave_half_sum(lrun[qb]);

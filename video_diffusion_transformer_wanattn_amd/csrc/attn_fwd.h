@@ -38,9 +38,9 @@
 //
 // Softmax is in base 2: the query is multiplied by scale * log2(e) when it is
 // loaded, so p = exp2(s - m) maps to v_exp_f32, and the subtraction of the row
-// reference m is folded into the QK^T product as one more MFMA k-step (a
-// K-side constant 1 against -m on the Q side, as two bf16 terms).  The
-// reference starts at the max of the first block and is only moved when a
+// reference m is folded into the QK^T product: its first k-step starts from an
+// accumulator tile holding -m instead of zero.  The O accumulators live in
+// AGPRs (the PV products are inline asm, see acc_fence).  The reference starts at the max of the first block and is only moved when a
 // lane's block sum of p exceeds 2^16 (some p above 2^12, or an overflow), which
 // makes the O rescale rare; the result is the same softmax (the final division
 // by the running sum uses the same reference point).
@@ -321,23 +321,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   };
   acc_fence();
   // Running softmax reference per query row, kept as a bias b = -m added to the
-  // scores inside the QK^T product: one extra MFMA k-step multiplies the K-side
-  // constant (1, 1) with the Q-side (hi, lo), the bias split into two bf16
-  // terms (b = hi + lo exactly in fp32, ~16 significant bits).  The scores come
-  // out of the product already shifted, and p = exp2(s) needs no subtraction.
+  // scores inside the QK^T product: the first k-step of the product starts
+  // from an accumulator tile holding b (every value a lane holds in S^T
+  // belongs to its own query column, so the tile is b repeated).  The scores
+  // come out of the product already shifted, and p = exp2(s) needs no
+  // subtraction; the tile only changes when the reference moves.
   float bias[2] = {0.0f, 0.0f}, lrun[2] = {0.0f, 0.0f};
-  bf16x8 qbias[2];
-  const bf16x8 kbias = __builtin_bit_cast(bf16x8, u32x4{hh == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u});
+  floatx16 btile[2];
   auto set_bias = [&](int qb, float b) __attribute__((always_inline)) {
-    const __bf16 hi = (__bf16)b;
-    const __bf16 lo = (__bf16)(b - (float)hi);
-    bias[qb] = (float)hi + (float)lo;
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 v;
-    v[0] = hi;
-    v[1] = lo;
-    const uint32_t w = hh == 0 ? __builtin_bit_cast(uint32_t, v) : 0u;
-    qbias[qb] = __builtin_bit_cast(bf16x8, u32x4{w, 0u, 0u, 0u});
+    bias[qb] = b;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) btile[qb][e] = b;
   };
   set_bias(0, 0.0f);
   set_bias(1, 0.0f);
@@ -385,11 +379,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
                                           0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto qk = [&]() __attribute__((always_inline)) {
-    const floatx16 z = {};
-    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias, qbias[0], z, 0, 0, 0);
-    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias, qbias[1], z, 0, 0, 0);
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[0][0], btile[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[1][0], btile[1], 0, 0, 0);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 1; kk < 8; ++kk) {
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], sacc[0], 0, 0, 0);
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
     }
@@ -538,18 +531,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     u32x4 pk1[2];
     float h1[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    {
-      const floatx16 z = {};
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias, qbias[0], z, 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias, qbias[1], z, 0, 0, 0);
-      load_vop(S, kb, 0, 0);
-      load_vop(S, kb, 0, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    load_vop(S, kb, 0, 0);
+    load_vop(S, kb, 0, 1);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], kk == 0 ? btile[0] : sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], kk == 0 ? btile[1] : sacc[1], 0, 0, 0);
       exp_pair(kk >> 2, 1, kk & 3, pk1[kk >> 2], h1[kk >> 2]);
       // keep the packed word here: it is only read after the check below,
       // and would otherwise be sunk past it

@@ -60,6 +60,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowBytes = 256;                 // one 128-wide bf16 row
 constexpr int kHalfTile = kBN * kRowBytes;     // 16 KiB: K' or V of one tile
 constexpr int kTileBytes = 2 * kHalfTile;      // 32 KiB
+constexpr int kVHalves = 4 * kHalfTile;        // V halves of the 4 stages start here (64 KiB)
 constexpr int kStages = 4;
 constexpr int kLdsBytes = kStages * kTileBytes;  // 128 KiB of 160
 constexpr int kLoadsPerTile = 8;               // global_load_lds per thread per tile (4 K + 4 V)
@@ -140,25 +141,15 @@ __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t
 
 template <bool ROPE, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
-  // one LDS object per stage: accesses to different stages then carry distinct
-  // alias scopes, so the compiler's wait for a stage's direct-to-LDS loads does
-  // not also wait for the loads still filling the other stages
-  __shared__ __attribute__((aligned(1024))) char st0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char st1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char st2[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char st3[kTileBytes];
-  // stage as a compile-time constant (main loop) or a run-time index (masked tail)
+  // LDS: the K' halves of the 4 stages in the first 64 KiB, their V halves in
+  // the second, so that every operand read is one base register (per lane)
+  // plus an immediate offset below 64 KiB (the ds_read offset field)
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  // K' half of a stage, as a compile-time constant (main loop) or a run-time
+  // index (masked tail); its V half is kVHalves further
   auto stage = [&](auto S) __attribute__((always_inline)) -> char* {
-    if constexpr (std::is_integral_v<decltype(S)>) {
-      const int s_ = S & (kStages - 1);
-      return s_ == 0 ? st0 : (s_ == 1 ? st1 : (s_ == 2 ? st2 : st3));
-    } else {
-      constexpr int s_ = decltype(S)::value;
-      if constexpr (s_ == 0) return st0;
-      else if constexpr (s_ == 1) return st1;
-      else if constexpr (s_ == 2) return st2;
-      else return st3;
-    }
+    if constexpr (std::is_integral_v<decltype(S)>) return lds + (S & (kStages - 1)) * kHalfTile;
+    else return lds + decltype(S)::value * kHalfTile;
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -219,14 +210,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     for (int i = 0; i < 4; ++i) {
       const int blk = 4 * wave + i;
       dma16(kt, koff_ld[i], st + blk * 1024);
-      dma16(vt, voff_ld[i], st + kHalfTile + blk * 1024);
+      dma16(vt, voff_ld[i], st + kVHalves + blk * 1024);
     }
   };
   // load n (0..7) of a full tile: K (n even) or V (n odd) rows of group n / 2
   auto issue_one = [&](auto S, int t, int n) __attribute__((always_inline)) {
     const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
     const int i = n >> 1, blk = 4 * wave + i;
-    if (n & 1) dma16(vbase + (size_t)t * kBN * rsb, voff_ld[i], st + kHalfTile + blk * 1024);
+    if (n & 1) dma16(vbase + (size_t)t * kBN * rsb, voff_ld[i], st + kVHalves + blk * 1024);
     else dma16(kbase + (size_t)t * kBN * rsb, koff_ld[i], st + blk * 1024);
   };
   auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {
@@ -243,7 +234,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
         const int kkey = min(t * kBN + k_slot(m), p.Nk - 1) - t * kBN;
         const int vkey = min(t * kBN + m, p.Nk - 1) - t * kBN;
         dma16(kt, (uint32_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m)), st + blk * 1024);
-        dma16(vt, (uint32_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m)), st + kHalfTile + blk * 1024);
+        dma16(vt, (uint32_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m)), st + kVHalves + blk * 1024);
       }
     }
   };
@@ -251,13 +242,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // zero every stage once: the look-ahead scoring of the block after the last
   // one reads a stage that may never have been filled
 #pragma unroll
-  for (int i = 0; i < kTileBytes / 16 / kThreads; ++i) {
-    const int o = 16 * (tid + i * kThreads);
-    *(u32x4*)(st0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4*)(st1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4*)(st2 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4*)(st3 + o) = u32x4{0, 0, 0, 0};
-  }
+  for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i) *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
   tile_barrier();
 
   // prefetch the first two tiles while the queries are loaded
@@ -342,13 +327,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // whose chunk 4 db + 2 (vg&1) + vq/2 is stored at 4 (db ^ vu) + 2 (vg&1) + vq/2.
   int koff[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) koff[kk] = r * kRowBytes + 16 * ((2 * kk + hh) ^ (r & 15));
+  for (int kk = 0; kk < 8; ++kk) {
+    koff[kk] = r * kRowBytes + 16 * ((2 * kk + hh) ^ (r & 15));
+    asm volatile("" : "+v"(koff[kk]));
+  }
   const int vg = lane >> 4, vu = (lane & 15) >> 2, vq = lane & 3;
   int voff[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
-    voff[db] = kHalfTile + (8 * (vg >> 1) + vu) * kRowBytes +
+    voff[db] = kVHalves + (8 * (vg >> 1) + vu) * kRowBytes +
                16 * (4 * (db ^ vu) + 2 * (vg & 1) + (vq >> 1)) + 8 * (vq & 1);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(voff[db]));
 
   bf16x8 kop[8];      // K' operands of the next block to score
   bf16x8 vop[4][2];   // V operands of the block being accumulated

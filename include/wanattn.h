@@ -37,8 +37,7 @@
  *    WANATTN_E_INVALID: null or misaligned pointer, sizes < 1, N != F*H*W,
  *    positions reaching 1024, an output overlapping an input, bad lengths.
  *    WANATTN_E_UNSUPPORTED: head_dim != 128, heads > WANATTN_MAX_HEADS, more
- *    batches than WANATTN_MAX_LEN_BATCH with a length array, more distinct
- *    theta values than the library keeps tables for.  WANATTN_E_HIP: a HIP call failed.
+ *    distinct theta values than the library keeps tables for.  WANATTN_E_HIP: a HIP call failed.
  *    wanattn_last_error() gives a thread-local text for the last failure.
  *  - Calls on different streams may run concurrently.
  */
@@ -55,7 +54,7 @@ extern "C" {
 #define WANATTN_VERSION 1
 #define WANATTN_HEAD_DIM 128
 #define WANATTN_MAX_POS 1024
-#define WANATTN_MAX_LEN_BATCH 256
+#define WANATTN_MAX_LEN_BATCH 256  /* batches per kernel launch (larger B: several launches) */
 #define WANATTN_MAX_HEADS 65536
 
 typedef enum wanattn_status {

@@ -102,8 +102,10 @@ def test_self_rejects_bad_lengths(lib):
     assert call_self(lib, B=2, lens=lens) == wa.E_INVALID
     lens = (ctypes.c_int32 * 2)(0, 5)
     assert call_self(lib, B=2, lens=lens) == wa.E_INVALID
-    big = (ctypes.c_int32 * 300)(*([24] * 300))
-    assert call_self(lib, B=300, lens=big, ws_bytes=1 << 28) == wa.E_UNSUPPORTED
+    # more batches than one launch takes: every entry is still checked (one
+    # bad length past the first launch's 256 is rejected before any launch)
+    big = (ctypes.c_int32 * 300)(*([24] * 299 + [25]))
+    assert call_self(lib, B=300, lens=big, ws_bytes=1 << 28) == wa.E_INVALID
 
 
 def test_self_kv_rejects(lib):

@@ -139,8 +139,6 @@ wanattn_status launched(const char* what) {
 
 wanattn_status check_lens(int32_t B, const int32_t* lens, int32_t maxlen, const char* name) {
   if (!lens) return WANATTN_OK;
-  if (B > WANATTN_MAX_LEN_BATCH)
-    return fail(WANATTN_E_UNSUPPORTED, "%s given for B=%d > %d", name, B, WANATTN_MAX_LEN_BATCH);
   for (int b = 0; b < B; ++b)
     if (lens[b] < 1 || lens[b] > maxlen)
       return fail(WANATTN_E_INVALID, "%s[%d]=%d outside [1, %d]", name, b, lens[b], maxlen);

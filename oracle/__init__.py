@@ -68,6 +68,9 @@ def _load():
         lib.orc_kv_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                     f64, f64, P, i32, P, P, i32]
         lib.orc_kv_rows.restype = i32
+        lib.orc_kv_rows_heads.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          i32, P, f64, P, i32, P, P, i32]
+        lib.orc_kv_rows_heads.restype = i32
         lib.orc_prologue_rows.argtypes = [P] * 11 + [i32, i32, i32, f64, f64, i32, P, P, P, P, i32]
         lib.orc_prologue_rows.restype = i32
         lib.orc_cross_rows.restype = i32
@@ -172,13 +175,15 @@ def self_rows(q, k, v, grid, rows=None, theta: float = 10000.0, scale: float | N
 
 
 def kv_rows(q, k, v, grid_q, kv_frame0: int = 0, rows=None, theta: float = 10000.0,
-            scale: float | None = None, kv_lens=None, threads: int | None = None):
+            scale: float | None = None, kv_lens=None, threads: int | None = None, theta_per_head=None):
     """A chunk of queries against a key/value cache (Self Forcing streaming).
 
     q: [B, Nq, heads, d] on the grid ``grid_q`` = (Fq, H, W, f0, h0, w0) (the
     chunk's first frame is f0); k, v: [B, Nkv, heads, d], Nkv / (H W) whole
     frames whose first frame is ``kv_frame0``, raw (the oracle rotates them).
-    Every key j < kv_lens[b] is visible.  Returns fp64 [B, len(rows), heads, d]."""
+    Every key j < kv_lens[b] is visible.  ``theta_per_head`` ([heads],
+    optional): multi-head RoPE jitter (``theta`` is then unused).
+    Returns fp64 [B, len(rows), heads, d]."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     B, Nq, heads, d = q.shape
     Nkv = k.shape[1]
@@ -191,6 +196,17 @@ def kv_rows(q, k, v, grid_q, kv_frame0: int = 0, rows=None, theta: float = 10000
         scale = 1.0 / np.sqrt(d)
     kvl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
     out = np.empty((B, rows.shape[0], heads, d), dtype=np.float64)
+    if theta_per_head is not None:
+        th = np.ascontiguousarray(theta_per_head, dtype=np.float64)
+        if th.shape != (heads,):
+            raise ValueError("theta_per_head needs one value per head")
+        rc = _load().orc_kv_rows_heads(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Nq, Nkv, heads, d, Fq,
+                                       H, W, int(f0), int(kv_frame0), int(h0), int(w0), th.ctypes.data, scale,
+                                       None if kvl is None else kvl.ctypes.data, rows.shape[0],
+                                       rows.ctypes.data, out.ctypes.data, _threads(threads))
+        if rc != 0:
+            raise ValueError("orc_kv_rows_heads rejected its arguments")
+        return out
     rc = _load().orc_kv_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Nq, Nkv, heads, d, Fq, H, W,
                              int(f0), int(kv_frame0), int(h0), int(w0), theta, scale,
                              None if kvl is None else kvl.ctypes.data, rows.shape[0], rows.ctypes.data,

@@ -385,10 +385,10 @@ int orc_self_rows_heads(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * from the raw inputs; every key j < kv_lens[b] is visible.
  * out: fp64 [B, nrows, heads, head_dim].
  */
-int orc_kv_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int Nq, int Nkv,
-                int heads, int head_dim, int Fq, int H, int W, int qf0, int kf0, int h0, int w0,
-                double theta, double scale, const int* kv_lens, int nrows, const int* rows,
-                double* out, int nthreads) {
+static int kv_rows_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int Nq, int Nkv,
+                        int heads, int head_dim, int Fq, int H, int W, int qf0, int kf0, int h0, int w0,
+                        double theta, const double* head_thetas, double scale, const int* kv_lens,
+                        int nrows, const int* rows, double* out, int nthreads) {
   if (B < 1 || Nq < 1 || Nkv < 1 || heads < 1 || head_dim < 2 || (head_dim % 2)) return 1;
   if (H < 1 || W < 1 || Nq != Fq * H * W || Nkv % (H * W)) return 1;
   for (int r = 0; r < nrows; ++r)
@@ -415,6 +415,7 @@ int orc_kv_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, 
   t.kh0 = h0;
   t.kw0 = w0;
   t.theta = theta;
+  t.head_theta = head_thetas;
   t.scale = scale;
   t.rope = 1;
   t.mask = 0;
@@ -424,6 +425,30 @@ int orc_kv_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, 
   t.rows = rows;
   t.out = out;
   return run_threads(&t, nthreads);
+}
+
+int orc_kv_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int Nq, int Nkv,
+                int heads, int head_dim, int Fq, int H, int W, int qf0, int kf0, int h0, int w0,
+                double theta, double scale, const int* kv_lens, int nrows, const int* rows,
+                double* out, int nthreads) {
+  return kv_rows_impl(q, k, v, B, Nq, Nkv, heads, head_dim, Fq, H, W, qf0, kf0, h0, w0, theta, 0, scale,
+                      kv_lens, nrows, rows, out, nthreads);
+}
+
+/*
+ * orc_kv_rows with multi-head RoPE jitter ([P3] "ルート2 · LoL", applied to
+ * the streamed, autoregressive setting it targets): head h rotates its
+ * queries and cached keys with its own base theta_heads[h] (finite, > 0).
+ */
+int orc_kv_rows_heads(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int Nq, int Nkv,
+                      int heads, int head_dim, int Fq, int H, int W, int qf0, int kf0, int h0, int w0,
+                      const double* theta_heads, double scale, const int* kv_lens, int nrows,
+                      const int* rows, double* out, int nthreads) {
+  if (!theta_heads || heads < 1) return 1;
+  for (int h = 0; h < heads; ++h)
+    if (!(theta_heads[h] > 0.0) || !isfinite(theta_heads[h])) return 1;
+  return kv_rows_impl(q, k, v, B, Nq, Nkv, heads, head_dim, Fq, H, W, qf0, kf0, h0, w0, 0.0, theta_heads,
+                      scale, kv_lens, nrows, rows, out, nthreads);
 }
 
 /*

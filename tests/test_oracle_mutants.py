@@ -43,6 +43,7 @@ MUTANTS = {
                                "t->head_theta ? t->head_theta[(hd + 1) % t->heads] : t->theta;"),
     "jitter_ignored": ("t->head_theta ? t->head_theta[hd] : t->theta;",
                        "t->head_theta ? t->head_theta[0] : t->theta;"),
+    "kv_jitter_one_base": ("h0, w0, 0.0, theta_heads,", "h0, w0, theta_heads[0], 0,"),
     "jitter_keys_unjittered": ("pos[1] + t->kh0, pos[2] + t->kw0, th);", "pos[1] + t->kh0, pos[2] + t->kw0, 1e4);"),
 }
 

@@ -416,16 +416,19 @@ def test_oracle_rejects_bad_arguments():
 # cached earlier chunks and to itself; [P1] ch. 4 "3D RoPE" for the positions)
 # ---------------------------------------------------------------------------
 
-def rotate_rows(x, F, H, W, off):
-    """numpy rotation of every token with explicit rotation matrices."""
+def rotate_rows(x, F, H, W, off, thetas=None):
+    """numpy rotation of every token with explicit rotation matrices (head h
+    with base thetas[h] when given)."""
     pos = grid_positions(F, H, W, off)
     xf = widen(x)
     out = np.empty_like(xf)
+    heads = x.shape[2]
+    thetas = [THETA] * heads if thetas is None else list(thetas)
     for n, p in enumerate(pos):
-        R = rotation_matrix(p)
+        Rs = [rotation_matrix(p, theta=th) for th in thetas]
         for b in range(x.shape[0]):
-            for h in range(x.shape[2]):
-                out[b, n, h] = R @ xf[b, n, h]
+            for h in range(heads):
+                out[b, n, h] = Rs[h] @ xf[b, n, h]
     return out
 
 
@@ -634,3 +637,38 @@ def test_jitter_common_theta_is_plain_rope_and_rejects():
     for bad in ([1e4], [1e4, 0.0], [1e4, -5.0], [1e4, float("nan")], [1e4, float("inf")]):
         with pytest.raises(ValueError):
             oracle.self_rows(q, k, v, grid, theta_per_head=bad)
+
+
+def test_kv_jitter_matches_explicit_rotations_and_library_sdpa():
+    # multi-head RoPE jitter in the streamed setting LoL targets: each head's
+    # queries and cached keys turn with that head's base
+    Fq, Fk, H, W = 2, 5, 3, 4
+    f0, kf0, h0, w0 = 7, 4, 1, 2
+    q = bf16((2, Fq * H * W, 3, 128), 82, 1, 1.5)
+    k, v = (bf16((2, Fk * H * W, 3, 128), 82, s, 1.5) for s in (2, 3))
+    qr = rotate_rows(q, Fq, H, W, (f0, h0, w0), JITTER_THETAS)
+    kr = rotate_rows(k, Fk, H, W, (kf0, h0, w0), JITTER_THETAS)
+    kvl = [60, 41]
+    got = oracle.kv_rows(q, k, v, (Fq, H, W, f0, h0, w0), kv_frame0=kf0, kv_lens=kvl,
+                         theta_per_head=JITTER_THETAS)
+    for b in range(2):
+        mask = np.zeros((Fq * H * W, Fk * H * W), dtype=bool)
+        mask[:, :kvl[b]] = True
+        want = sdpa(qr[b:b + 1], kr[b:b + 1], widen(v)[b:b + 1], mask)
+        np.testing.assert_allclose(got[b:b + 1], want, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.kv_rows(q, k, v, (Fq, H, W, f0, h0, w0), theta_per_head=[1e4, 1e4, 0.0])
+
+
+def test_kv_jitter_chunks_equal_block_causal_jitter_rows():
+    F, H, W, C = 6, 3, 4, 2
+    HW = H * W
+    q, k, v = (bf16((1, F * HW, 3, 128), 83, s, 1.5) for s in (1, 2, 3))
+    full = oracle.self_rows(q, k, v, (F, H, W), block_causal=True, chunk_frames=C,
+                            theta_per_head=JITTER_THETAS)
+    for c in range(F // C):
+        rows = slice(c * C * HW, (c + 1) * C * HW)
+        n = (c + 1) * C * HW
+        got = oracle.kv_rows(q[:, rows], k[:, :n], v[:, :n], (C, H, W, c * C, 0, 0), kv_frame0=0,
+                             theta_per_head=JITTER_THETAS)
+        np.testing.assert_allclose(got, full[:, rows], rtol=0, atol=1e-12)

@@ -179,10 +179,11 @@ def cfg_leg(torch, wa, wl, q, k, v, kc, vc, steps, warmup):
             "cross_tflops_visible": round(f_cross / (c_ms * 1e-3) / 1e12, 2)}
 
 
-def kv_stream_leg(torch, seeded, wa, steps, warmup):
+def kv_stream_leg(torch, seeded, wa, steps, warmup, jitter=False):
     """One streaming step of Self Forcing: rotate the new chunk's keys into the
     cache (wanattn_rope3d) and attend the chunk's queries to the whole cache
-    (wanattn_self_kv).  Times both with HIP events on the launch stream."""
+    (wanattn_self_kv).  Times both with HIP events on the launch stream.
+    jitter: with multi-head RoPE jitter (per-head tables built once)."""
     import numpy as np
     wl = seeded.WORKLOADS["wan14b_480p_165f_causal"]
     t = seeded.workload_tensors(wl, seed=0, cross=False)
@@ -191,17 +192,18 @@ def kv_stream_leg(torch, seeded, wa, steps, warmup):
     dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
     q = dev(t["q"][:, c0 * hw:])
     k_raw, v = dev(t["k"]), dev(t["v"])
-    kc = wa.rope3d(k_raw, (wl.F, wl.H, wl.W))               # cache of the earlier chunks, rotated once
+    tables = wa.rope_tables(seeded.jitter_thetas(wl.heads, seed=0)) if jitter else None
+    kc = wa.rope3d(k_raw, (wl.F, wl.H, wl.W), tables=tables)   # cache of the earlier chunks, rotated once
     new_k = k_raw[:, c0 * hw:]
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        wa.rope3d(new_k, (wl.chunk_frames, wl.H, wl.W), offsets=(c0, 0, 0), out=kc[:, c0 * hw:])
+        wa.rope3d(new_k, (wl.chunk_frames, wl.H, wl.W), offsets=(c0, 0, 0), out=kc[:, c0 * hw:], tables=tables)
         if ev is not None:
             ev[1].record(stream)
-        wa.self_attention_kv(q, kc, v, (wl.chunk_frames, wl.H, wl.W), offsets=(c0, 0, 0), out=o)
+        wa.self_attention_kv(q, kc, v, (wl.chunk_frames, wl.H, wl.W), offsets=(c0, 0, 0), out=o, tables=tables)
         if ev is not None:
             ev[2].record(stream)
     for _ in range(warmup):
@@ -215,7 +217,7 @@ def kv_stream_leg(torch, seeded, wa, steps, warmup):
     attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     nq, nkv = q.shape[1], k_raw.shape[1]
     f = 4 * wl.head_dim * wl.heads * nq * nkv
-    log(f"kv stream: chunk {nq} x cache {nkv} x {wl.heads} heads: attention {attn_ms:.3f} ms, "
+    log(f"kv stream{' (jitter)' if jitter else ''}: chunk {nq} x cache {nkv} x {wl.heads} heads: attention {attn_ms:.3f} ms, "
         f"cache append {rope_ms:.3f} ms")
     return {"workload": "wan14b_480p_165f_causal, last chunk (frames 39-41) against the 42-frame cache",
             "q_tokens": nq, "kv_tokens": nkv, "heads": wl.heads, "flops": f,
@@ -431,6 +433,8 @@ def main():
     }
     if args.kv_stream:
         result["kv_stream"] = kv_stream_leg(torch, seeded, wa, args.steps, args.warmup)
+        if args.jitter:
+            result["kv_stream_jitter"] = kv_stream_leg(torch, seeded, wa, args.steps, args.warmup, jitter=True)
     if args.cfg:
         del o_self, o_cross
         result["cfg_batch"] = cfg_leg(torch, wa, wl, q, k, v, kc, vc, args.steps, args.warmup)

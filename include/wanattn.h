@@ -161,6 +161,37 @@ wanattn_status wanattn_self_kv(const void* q, const void* k_cache, const void* v
                                const int32_t* kv_lens, void* stream);
 
 /*
+ * [P3] "ルート2 · LoL" multi-head RoPE jitter in the streamed setting
+ * ("ルート3 · Self Forcing"): per-head rotary tables, head h with its own
+ * base theta_per_head[h] (the reading of wanattn_self_jitter), built once by
+ * the caller and used by the two streaming calls below.
+ *
+ * wanattn_rope_tables: builds the tables of `heads` heads into `tables`
+ *   (caller-owned device memory, 16-byte aligned, at least
+ *   wanattn_rope_tables_bytes(heads) bytes = 768 KiB per head), in fp64 on the
+ *   device, rounded to fp32; enqueued on `stream`.  theta_per_head: HOST
+ *   array [heads], each finite and > 0; heads <= WANATTN_MAX_JITTER_HEADS.
+ * wanattn_rope3d_tables: wanattn_rope3d with head h rotated by table h
+ *   (e.g. a new chunk's keys appended to a jittered cache).
+ * wanattn_self_kv_tables: wanattn_self_kv whose queries are rotated by the
+ *   per-head tables; the cache keys must have been rotated with the same
+ *   tables (wanattn_rope3d_tables).
+ * `tables` must hold tables built for at least `heads` heads (only their
+ * size can be checked) and must not overlap an output.  Errors and numerics
+ * otherwise as wanattn_rope3d / wanattn_self_kv.
+ */
+size_t wanattn_rope_tables_bytes(int32_t heads);
+wanattn_status wanattn_rope_tables(const double* theta_per_head, int32_t heads, void* tables,
+                                   size_t tables_bytes, void* stream);
+wanattn_status wanattn_rope3d_tables(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
+                                     int32_t head_dim, const wanattn_grid3d* grid, const void* tables,
+                                     size_t tables_bytes, void* stream);
+wanattn_status wanattn_self_kv_tables(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                      int32_t B, int32_t Nq, int32_t Nkv, int32_t heads, int32_t head_dim,
+                                      const wanattn_grid3d* grid_q, const void* tables, size_t tables_bytes,
+                                      float scale, const int32_t* kv_lens, void* stream);
+
+/*
  * [P2] cross attention, called as cross_attn(x, context, context_lens) in
  * [P1] ch. 4: o = softmax(q k_ctx^T * scale) v_ctx, no rotary embedding.
  * q, o: [B, N, heads, 128]; k_ctx, v_ctx: [B, M, heads, 128] (M text tokens,

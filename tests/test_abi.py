@@ -183,6 +183,52 @@ def test_self_jitter_workspace_and_rejects(lib):
     assert lib.wanattn_last_error()
 
 
+def test_rope_tables_calls_reject():
+    tab = 3 * 1024 * 32 * 8
+    assert lib_bytes(3) == 3 * tab and lib_bytes(0) == 0 and lib_bytes(257) == 0
+    lib = wa.load_library()
+    th = (ctypes.c_double * 3)(1e4, 5e2, 2e5)
+    T = ctypes.c_void_p(6 << 30)
+    # building
+    assert lib.wanattn_rope_tables(None, 3, T, 3 * tab, None) == wa.E_INVALID
+    assert lib.wanattn_rope_tables((ctypes.c_double * 3)(1e4, -1.0, 1e4), 3, T, 3 * tab, None) == wa.E_INVALID
+    assert lib.wanattn_rope_tables((ctypes.c_double * 257)(*([1e4] * 257)), 257, T, 257 * tab, None) == wa.E_UNSUPPORTED
+    assert lib.wanattn_rope_tables(th, 0, T, 3 * tab, None) == wa.E_INVALID
+    assert lib.wanattn_rope_tables(th, 3, None, 3 * tab, None) == wa.E_INVALID
+    assert lib.wanattn_rope_tables(th, 3, ctypes.c_void_p((6 << 30) + 8), 3 * tab, None) == wa.E_INVALID
+    assert lib.wanattn_rope_tables(th, 3, T, 3 * tab - 1, None) == wa.E_INVALID
+
+    # rotating with them
+    def rope(x=A, y=O, B=1, N=24, heads=3, d=128, grid=None, t=T, tb=3 * tab):
+        return lib.wanattn_rope3d_tables(x, y, B, N, heads, d, grid if grid is not None else g(2, 3, 4), t, tb, None)
+    assert rope(x=None) == wa.E_INVALID
+    assert rope(t=None) == wa.E_INVALID
+    assert rope(tb=2 * tab) == wa.E_INVALID                     # tables for fewer heads
+    assert rope(y=ctypes.c_void_p((6 << 30) + 4096)) == wa.E_INVALID  # y inside the tables
+    assert rope(N=23) == wa.E_INVALID
+    assert rope(d=64) == wa.E_UNSUPPORTED
+    assert rope(heads=300, tb=300 * tab) == wa.E_UNSUPPORTED
+
+    # attending with them
+    def kv(q=A, k=B_, v=C, o=O, B=1, Nq=24, Nkv=60, heads=3, d=128, grid=None, t=T, tb=3 * tab, scale=0.088,
+           lens=None):
+        return lib.wanattn_self_kv_tables(q, k, v, o, B, Nq, Nkv, heads, d,
+                                          grid if grid is not None else g(2, 3, 4, 3, 0, 0), t, tb, scale, lens,
+                                          None)
+    assert kv(t=None) == wa.E_INVALID
+    assert kv(tb=tab) == wa.E_INVALID
+    assert kv(o=ctypes.c_void_p(6 << 30)) == wa.E_INVALID       # o on the tables
+    assert kv(Nkv=58) == wa.E_INVALID
+    assert kv(q=None) == wa.E_INVALID
+    assert kv(lens=(ctypes.c_int32 * 1)(61)) == wa.E_INVALID
+    assert kv(heads=300, tb=300 * tab) == wa.E_UNSUPPORTED
+    assert lib.wanattn_last_error()
+
+
+def lib_bytes(heads):
+    return wa.load_library().wanattn_rope_tables_bytes(heads)
+
+
 GEMM_WS = 128 << 20  # hipBLASLt's share of the prologue workspace
 
 

@@ -75,3 +75,48 @@ def test_jitter_errors():
         wa.self_attention(q, q.clone(), q.clone(), (2, 3, 4), theta_per_head=[1e4])
     with pytest.raises(wa.WanattnError):
         wa.self_attention(q, q.clone(), q.clone(), (2, 3, 4), theta_per_head=[1e4, -1.0])
+
+
+def test_jitter_kv_stream_chunk_by_chunk():
+    # the streamed setting LoL targets: per-head tables built once, every new
+    # chunk's keys appended to the cache with them, each chunk's queries
+    # against the cache so far (6 frames of 9 x 10 tokens, chunks of 2 frames)
+    F, H, W, C, B, heads = 6, 9, 10, 2, 2, 3
+    HW = H * W
+    thetas = [10000.0, 500.0, 2.0e5]
+    q, k = (gen((B, F * HW, heads, 128), 92, s, 1.5) for s in (1, 2))
+    v = gen((B, F * HW, heads, 128), 92, 3, 0.5)
+    tables = wa.rope_tables(thetas)
+    dk = to_dev(k)
+    cache = torch.empty_like(dk)
+    dv = to_dev(v)
+    for c in range(F // C):
+        rows = slice(c * C * HW, (c + 1) * C * HW)
+        n = (c + 1) * C * HW
+        cache[:, rows] = wa.rope3d(dk[:, rows].contiguous(), (C, H, W), offsets=(c * C, 0, 0), tables=tables)
+        qc = np.ascontiguousarray(q[:, rows])
+        o = wa.self_attention_kv(to_dev(qc), cache[:, :n].contiguous(), dv[:, :n].contiguous(), (C, H, W),
+                                 offsets=(c * C, 0, 0), tables=tables)
+        torch.cuda.synchronize()
+        ref = oracle.kv_rows(qc, k[:, :n], v[:, :n], (C, H, W, c * C, 0, 0), kv_frame0=0, theta_per_head=thetas)
+        assert_parity(from_dev(o), ref, what=f"jitter kv chunk {c}")
+
+
+def test_jitter_kv_stream_last_chunk_165_frames():
+    # the 165-frame workload's last 3-frame chunk (4,680 queries) against its
+    # 42-frame cache (65,520 keys), 40 heads, seeded per-head bases
+    wl = seeded.WORKLOADS["wan14b_480p_165f_causal"]
+    t = seeded.workload_tensors(wl, seed=0, cross=False)
+    thetas = seeded.jitter_thetas(wl.heads, seed=0)
+    hw = wl.H * wl.W
+    c0 = wl.F - wl.chunk_frames
+    tables = wa.rope_tables(thetas)
+    cache = wa.rope3d(to_dev(t["k"]), (wl.F, wl.H, wl.W), tables=tables)
+    qc = np.ascontiguousarray(t["q"][:, c0 * hw:])
+    o = wa.self_attention_kv(to_dev(qc), cache, to_dev(t["v"]), (wl.chunk_frames, wl.H, wl.W),
+                             offsets=(c0, 0, 0), tables=tables)
+    torch.cuda.synchronize()
+    rows = seeded.sample_rows(qc.shape[1], 16, seed=6)
+    ref = oracle.kv_rows(qc, t["k"], t["v"], (wl.chunk_frames, wl.H, wl.W, c0, 0, 0), kv_frame0=0, rows=rows,
+                         theta_per_head=thetas)
+    assert_parity(from_dev(o)[:, rows], ref, what="jitter kv 4680 x 65520 sampled")

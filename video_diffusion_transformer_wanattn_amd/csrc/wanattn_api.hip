@@ -275,6 +275,88 @@ wanattn_status self_launch(const void* q, const void* k, const void* v, void* o,
 
 size_t jitter_table_bytes(int heads) { return (size_t)heads * kTabEntries * sizeof(float2); }
 
+wanattn_status check_head_thetas(const double* theta_per_head, int32_t heads) {
+  if (heads < 1) return fail(WANATTN_E_INVALID, "heads must be >= 1");
+  if (heads > kMaxJitterHeads)
+    return fail(WANATTN_E_UNSUPPORTED, "heads=%d above %d for per-head tables", heads, kMaxJitterHeads);
+  if (!theta_per_head) return fail(WANATTN_E_INVALID, "theta_per_head is NULL");
+  for (int h = 0; h < heads; ++h)
+    if (!(theta_per_head[h] > 0.0) || !std::isfinite(theta_per_head[h]))
+      return fail(WANATTN_E_INVALID, "theta_per_head[%d] must be finite and > 0", h);
+  return WANATTN_OK;
+}
+
+// per-head tables for checked bases into `tab` (heads * kTabEntries entries)
+wanattn_status build_head_tables(const double* theta_per_head, int32_t heads, float2* tab, hipStream_t stream) {
+  TableParams tp;
+  memset(&tp, 0, sizeof tp);
+  tp.tab = tab;
+  tp.heads = heads;
+  for (int h = 0; h < heads; ++h) tp.theta[h] = theta_per_head[h];
+  const long long total = (long long)heads * kTabEntries;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, tp);
+  return launched("rope_table");
+}
+
+// a caller's table set: heads tables of kTabEntries entries
+wanattn_status check_tables(const void* tables, size_t tables_bytes, int32_t heads) {
+  if (!tables) return fail(WANATTN_E_INVALID, "tables is NULL");
+  if (!aligned16(tables)) return fail(WANATTN_E_INVALID, "tables must be 16-byte aligned");
+  if (heads > kMaxJitterHeads)
+    return fail(WANATTN_E_UNSUPPORTED, "heads=%d above %d for per-head tables", heads, kMaxJitterHeads);
+  if (tables_bytes < jitter_table_bytes(heads))
+    return fail(WANATTN_E_INVALID, "tables has %zu bytes, %zu needed for %d heads", tables_bytes,
+                jitter_table_bytes(heads), heads);
+  return WANATTN_OK;
+}
+
+// checks of the KV-cache streaming call (the table is checked by the caller)
+wanattn_status check_kv(const void* q, const void* k_cache, const void* v_cache, const void* o, int32_t B,
+                        int32_t Nq, int32_t Nkv, int32_t heads, int32_t head_dim, const wanattn_grid3d* grid_q,
+                        float scale, const int32_t* kv_lens) {
+  if (!q || !k_cache || !v_cache || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, Nq, heads, head_dim));
+  WA_TRY(check_tensor_sizes(B, Nkv, heads, head_dim));
+  WA_TRY(check_grid(grid_q, Nq));
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
+  const long long hw = (long long)grid_q->H * grid_q->W;
+  if (Nkv % hw != 0) return fail(WANATTN_E_INVALID, "Nkv=%d is not whole frames of %lld tokens", Nkv, hw);
+  const size_t qbytes = (size_t)B * Nq * heads * kHeadDim * 2, kbytes = (size_t)B * Nkv * heads * kHeadDim * 2;
+  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k_cache, kbytes) || overlap(o, qbytes, v_cache, kbytes))
+    return fail(WANATTN_E_INVALID, "o overlaps an input");
+  return check_lens(B, kv_lens, Nkv, "kv_lens");
+}
+
+// one chunk of queries against the rotated cache, head h's table at tab + h * hstride
+wanattn_status kv_launch(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t B, int32_t Nq,
+                         int32_t Nkv, int32_t heads, const wanattn_grid3d* grid_q, const float2* tab,
+                         long long hstride, float scale, const int32_t* kv_lens, hipStream_t stream) {
+  AttnParams p;
+  memset(&p, 0, sizeof p);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k_cache;
+  p.v = (const uint16_t*)v_cache;
+  p.o = (uint16_t*)o;
+  p.tab = tab;
+  p.tab_hstride = hstride;
+  p.N = Nq;
+  p.Nk = Nkv;
+  p.heads = heads;
+  p.qscale = scale * 1.4426950408889634f;
+  p.H = grid_q->H;
+  p.W = grid_q->W;
+  p.f0 = grid_q->f0;
+  p.h0 = grid_q->h0;
+  p.w0 = grid_q->w0;
+  p.inv_hw = 1.0 / ((double)grid_q->H * grid_q->W);
+  p.inv_w = 1.0 / (double)grid_q->W;
+  return launch_attn<true, false>(p, B, kv_lens, stream);
+}
+
 // ---- q/k/v projections: plain bf16 GEMMs in hipBLASLt ---------------------
 
 constexpr size_t kGemmWorkspace = size_t(128) << 20;  // hipBLASLt's share of the prologue workspace
@@ -445,26 +527,12 @@ wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* stream) {
   t_err[0] = 0;
   WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
-  if (heads > kMaxJitterHeads)
-    return fail(WANATTN_E_UNSUPPORTED, "heads=%d above %d for per-head tables", heads, kMaxJitterHeads);
-  if (!theta_per_head) return fail(WANATTN_E_INVALID, "theta_per_head is NULL");
-  for (int h = 0; h < heads; ++h)
-    if (!(theta_per_head[h] > 0.0) || !std::isfinite(theta_per_head[h]))
-      return fail(WANATTN_E_INVALID, "theta_per_head[%d] must be finite and > 0", h);
+  WA_TRY(check_head_thetas(theta_per_head, heads));
   const size_t tbytes = jitter_table_bytes(heads);
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
   WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
                     workspace_bytes, tbytes + bytes));
-  TableParams tp;
-  memset(&tp, 0, sizeof tp);
-  tp.tab = (float2*)workspace;
-  tp.heads = heads;
-  for (int h = 0; h < heads; ++h) tp.theta[h] = theta_per_head[h];
-  const long long total = (long long)heads * kTabEntries;
-  long long blocks = (total + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, tp);
-  WA_TRY(launched("rope_table"));
+  WA_TRY(build_head_tables(theta_per_head, heads, (float2*)workspace, (hipStream_t)stream));
   return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens,
                      (char*)workspace + tbytes, (const float2*)workspace, kTabEntries, (hipStream_t)stream);
 }
@@ -474,41 +542,53 @@ wanattn_status wanattn_self_kv(const void* q, const void* k_cache, const void* v
                                const wanattn_grid3d* grid_q, double theta, float scale,
                                const int32_t* kv_lens, void* stream) {
   t_err[0] = 0;
-  if (!q || !k_cache || !v_cache || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
-  WA_TRY(check_tensor_sizes(B, Nq, heads, head_dim));
-  WA_TRY(check_tensor_sizes(B, Nkv, heads, head_dim));
-  WA_TRY(check_grid(grid_q, Nq));
+  WA_TRY(check_kv(q, k_cache, v_cache, o, B, Nq, Nkv, heads, head_dim, grid_q, scale, kv_lens));
   WA_TRY(check_theta(theta));
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
-  const long long hw = (long long)grid_q->H * grid_q->W;
-  if (Nkv % hw != 0) return fail(WANATTN_E_INVALID, "Nkv=%d is not whole frames of %lld tokens", Nkv, hw);
-  const size_t qbytes = (size_t)B * Nq * heads * kHeadDim * 2, kbytes = (size_t)B * Nkv * heads * kHeadDim * 2;
-  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k_cache, kbytes) || overlap(o, qbytes, v_cache, kbytes))
-    return fail(WANATTN_E_INVALID, "o overlaps an input");
-  WA_TRY(check_lens(B, kv_lens, Nkv, "kv_lens"));
-  AttnParams p;
-  memset(&p, 0, sizeof p);
   const float2* tab = nullptr;
   WA_TRY(table_for(theta, &tab));
-  p.q = (const uint16_t*)q;
-  p.k = (const uint16_t*)k_cache;
-  p.v = (const uint16_t*)v_cache;
-  p.o = (uint16_t*)o;
-  p.tab = tab;
-  p.N = Nq;
-  p.Nk = Nkv;
-  p.heads = heads;
-  p.qscale = scale * 1.4426950408889634f;
-  p.H = grid_q->H;
-  p.W = grid_q->W;
-  p.f0 = grid_q->f0;
-  p.h0 = grid_q->h0;
-  p.w0 = grid_q->w0;
-  p.inv_hw = 1.0 / ((double)grid_q->H * grid_q->W);
-  p.inv_w = 1.0 / (double)grid_q->W;
-  return launch_attn<true, false>(p, B, kv_lens, (hipStream_t)stream);
+  return kv_launch(q, k_cache, v_cache, o, B, Nq, Nkv, heads, grid_q, tab, 0, scale, kv_lens,
+                   (hipStream_t)stream);
+}
+
+size_t wanattn_rope_tables_bytes(int32_t heads) {
+  if (heads < 1 || heads > kMaxJitterHeads) return 0;
+  return jitter_table_bytes(heads);
+}
+
+wanattn_status wanattn_rope_tables(const double* theta_per_head, int32_t heads, void* tables,
+                                   size_t tables_bytes, void* stream) {
+  t_err[0] = 0;
+  WA_TRY(check_head_thetas(theta_per_head, heads));
+  WA_TRY(check_tables(tables, tables_bytes, heads));
+  return build_head_tables(theta_per_head, heads, (float2*)tables, (hipStream_t)stream);
+}
+
+wanattn_status wanattn_rope3d_tables(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
+                                     int32_t head_dim, const wanattn_grid3d* grid, const void* tables,
+                                     size_t tables_bytes, void* stream) {
+  t_err[0] = 0;
+  if (!x || !y) return fail(WANATTN_E_INVALID, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(y)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  WA_TRY(check_grid(grid, N));
+  WA_TRY(check_tables(tables, tables_bytes, heads));
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2, tbytes = jitter_table_bytes(heads);
+  if (x != y && overlap(x, bytes, y, bytes)) return fail(WANATTN_E_INVALID, "y partially overlaps x");
+  if (overlap(tables, tbytes, y, bytes)) return fail(WANATTN_E_INVALID, "y overlaps the tables");
+  return rope3d_launch(x, y, B, N, heads, grid, (const float2*)tables, kTabEntries, (hipStream_t)stream);
+}
+
+wanattn_status wanattn_self_kv_tables(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                      int32_t B, int32_t Nq, int32_t Nkv, int32_t heads, int32_t head_dim,
+                                      const wanattn_grid3d* grid_q, const void* tables, size_t tables_bytes,
+                                      float scale, const int32_t* kv_lens, void* stream) {
+  t_err[0] = 0;
+  WA_TRY(check_kv(q, k_cache, v_cache, o, B, Nq, Nkv, heads, head_dim, grid_q, scale, kv_lens));
+  WA_TRY(check_tables(tables, tables_bytes, heads));
+  const size_t qbytes = (size_t)B * Nq * heads * kHeadDim * 2;
+  if (overlap(o, qbytes, tables, jitter_table_bytes(heads))) return fail(WANATTN_E_INVALID, "o overlaps the tables");
+  return kv_launch(q, k_cache, v_cache, o, B, Nq, Nkv, heads, grid_q, (const float2*)tables, kTabEntries, scale,
+                   kv_lens, (hipStream_t)stream);
 }
 
 wanattn_status wanattn_cross(const void* q, const void* k_ctx, const void* v_ctx, void* o,

@@ -23,7 +23,8 @@ MAX_LEN_BATCH = 256
 MAX_JITTER_HEADS = 256
 
 EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wanattn_self_jitter",
-           "wanattn_self_jitter_workspace_bytes", "wanattn_self_kv",
+           "wanattn_self_jitter_workspace_bytes", "wanattn_self_kv", "wanattn_rope_tables_bytes",
+           "wanattn_rope_tables", "wanattn_rope3d_tables", "wanattn_self_kv_tables",
            "wanattn_cross", "wanattn_prologue", "wanattn_prologue_workspace_bytes", "wanattn_prepare",
            "wanattn_status_string", "wanattn_last_error", "wanattn_version")
 
@@ -67,6 +68,15 @@ def load_library(path: str = LIB_PATH):
     lib.wanattn_self_jitter_workspace_bytes.restype = ctypes.c_size_t
     lib.wanattn_self_kv.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, G, f64, f32, P, P]
     lib.wanattn_self_kv.restype = ctypes.c_int
+    lib.wanattn_rope_tables_bytes.argtypes = [i32]
+    lib.wanattn_rope_tables_bytes.restype = ctypes.c_size_t
+    lib.wanattn_rope_tables.argtypes = [P, i32, P, ctypes.c_size_t, P]
+    lib.wanattn_rope_tables.restype = ctypes.c_int
+    lib.wanattn_rope3d_tables.argtypes = [P, P, i32, i32, i32, i32, G, P, ctypes.c_size_t, P]
+    lib.wanattn_rope3d_tables.restype = ctypes.c_int
+    lib.wanattn_self_kv_tables.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, G, P, ctypes.c_size_t, f32, P,
+                                           P]
+    lib.wanattn_self_kv_tables.restype = ctypes.c_int
     lib.wanattn_cross.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, P, P]
     lib.wanattn_cross.restype = ctypes.c_int
     lib.wanattn_prologue.argtypes = [P] * 14 + [i32, i32, i32, f32, f32, P, ctypes.c_size_t, P]
@@ -131,8 +141,31 @@ def _dims(t, *others):
     return tuple(int(x) for x in t.shape)
 
 
-def rope3d(x, grid, theta: float = 10000.0, offsets=(0, 0, 0), out=None, stream=None):
-    """3D RoPE of x ([B, N, heads, 128] bf16); out may be x (in place)."""
+def _tables(tables):
+    if not tables.is_cuda or not tables.is_contiguous():
+        raise ValueError("tables must be a contiguous GPU tensor (see rope_tables)")
+    return _ptr(tables), tables.numel() * tables.element_size()
+
+
+def rope_tables(theta_per_head, out=None, stream=None):
+    """Per-head rotary tables (head h with RoPE base theta_per_head[h]) for
+    the streamed jitter calls; a uint8 GPU tensor unless ``out`` is given."""
+    import torch
+    lib = load_library()
+    th = [float(x) for x in theta_per_head]
+    heads = len(th)
+    need = int(lib.wanattn_rope_tables_bytes(heads))
+    if out is None:
+        out = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    ptr, nbytes = _tables(out)
+    _raise_on(lib.wanattn_rope_tables((ctypes.c_double * max(heads, 1))(*th), heads, ptr, nbytes,
+                                      _stream(stream)))
+    return out
+
+
+def rope3d(x, grid, theta: float = 10000.0, offsets=(0, 0, 0), out=None, stream=None, tables=None):
+    """3D RoPE of x ([B, N, heads, 128] bf16); out may be x (in place).
+    ``tables`` (from rope_tables): rotate head h with its own table instead."""
     import torch
     lib = load_library()
     if out is None:
@@ -141,6 +174,11 @@ def rope3d(x, grid, theta: float = 10000.0, offsets=(0, 0, 0), out=None, stream=
     if tuple(out.shape) != tuple(x.shape):
         raise ValueError("out must have the shape of x")
     g = _grid(grid, offsets)
+    if tables is not None:
+        tp, tb = _tables(tables)
+        _raise_on(lib.wanattn_rope3d_tables(_ptr(x), _ptr(out), B, N, heads, d, ctypes.byref(g), tp, tb,
+                                            _stream(stream)))
+        return out
     _raise_on(lib.wanattn_rope3d(_ptr(x), _ptr(out), B, N, heads, d, ctypes.byref(g), float(theta),
                                  _stream(stream)))
     return out
@@ -204,10 +242,12 @@ def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = 
 
 
 def self_attention_kv(q, k_cache, v_cache, grid_q, theta: float = 10000.0, scale: float | None = None,
-                      kv_lens=None, offsets=(0, 0, 0), out=None, stream=None):
+                      kv_lens=None, offsets=(0, 0, 0), out=None, stream=None, tables=None):
     """One chunk of queries (grid_q frames at RoPE offsets ``offsets``) against a
     key/value cache of whole frames; k_cache holds keys already rotated by
-    their own positions (see rope3d).  Every key j < kv_lens[b] is visible."""
+    their own positions (see rope3d).  Every key j < kv_lens[b] is visible.
+    ``tables`` (from rope_tables): per-head RoPE tables (multi-head jitter;
+    the cache must have been rotated with the same tables)."""
     import torch
     lib = load_library()
     if out is None:
@@ -223,6 +263,12 @@ def self_attention_kv(q, k_cache, v_cache, grid_q, theta: float = 10000.0, scale
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     g = _grid(grid_q, offsets)
+    if tables is not None:
+        tp, tb = _tables(tables)
+        _raise_on(lib.wanattn_self_kv_tables(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Nq, Nkv, heads,
+                                             d, ctypes.byref(g), tp, tb, float(scale), _lens(kv_lens, B),
+                                             _stream(stream)))
+        return out
     _raise_on(lib.wanattn_self_kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Nq, Nkv, heads, d,
                                   ctypes.byref(g), float(theta), float(scale), _lens(kv_lens, B),
                                   _stream(stream)))

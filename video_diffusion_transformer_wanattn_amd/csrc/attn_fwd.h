@@ -63,7 +63,6 @@ constexpr int kTileBytes = 2 * kHalfTile;      // 32 KiB
 constexpr int kVHalves = 4 * kHalfTile;        // V halves of the 4 stages start here (64 KiB)
 constexpr int kStages = 4;
 constexpr int kLdsBytes = kStages * kTileBytes;  // 128 KiB of 160
-constexpr int kLoadsPerTile = 8;               // global_load_lds per thread per tile (4 K + 4 V)
 constexpr float kLazySum = 65536.0f;           // lane partial block sum that moves the reference
 
 struct AttnParams {

@@ -611,24 +611,39 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   }
   for (; t < nt; ++t) tile_step(t, t + 1, t + 3, Mask{}, t);
 
-  // ---- epilogue: O = O^T / l, bf16; lane holds d = 32 db + 8 g4 + 4 hh + 0..3
+  // ---- epilogue: O = O^T / l, bf16.  A lane holds d = 32 db + 8 g4 + 4 hh + 0..3
+  // of one query; each wave writes its 64 rows into LDS (chunks XOR-swizzled
+  // by row) and reads them back as whole 256-byte rows, so that the stores to
+  // O are 16 bytes per lane and 1 KiB (4 full rows) per instruction instead
+  // of 8-byte pieces of 32 rows.  Every wave is past its last LDS operand read
+  // and no tile load is in flight after the barrier.
   acc_fence();
+  wait_vm<0>();
+  tile_barrier();
+  char* orows = lds + wave * (64 * kRowBytes);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float inv = 1.0f / wave_half_sum(lrun[qb]);
-    const int i = i0 + wave * 64 + qb * 32 + r;
-    if (i < p.N) {
-      uint16_t* dst = p.o + ((size_t)b * p.N + i) * row_stride + (size_t)head * kHeadDim;
+    const int row = qb * 32 + r;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv);
-          w[1] = pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv);
-          *(u32x2*)(dst + 32 * db + 8 * g4 + 4 * hh) = w;
-        }
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv);
+        w[1] = pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv);
+        *(u32x2*)(orows + row * kRowBytes + 16 * ((4 * db + g4) ^ (row & 15)) + 8 * hh) = w;
+      }
+  }
+  const int sr = lane >> 4, sc = lane & 15;
+  const int irow0 = i0 + wave * 64 + sr;
+  uint16_t* dst = p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int row = 4 * it + sr;
+    const u32x4 w = *(const u32x4*)(orows + row * kRowBytes + 16 * (sc ^ (row & 15)));
+    if (irow0 + 4 * it < p.N) *(u32x4*)dst = w;
+    dst += 4 * row_stride;
   }
 }
 

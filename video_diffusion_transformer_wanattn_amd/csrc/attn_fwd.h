@@ -238,11 +238,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  // zero every stage once: the look-ahead scoring of the block after the last
-  // one reads a stage that may never have been filled
+  // the look-ahead scoring of the block after the last one reads the next
+  // stage: with fewer tiles than stages that stage was never filled, so zero
+  // the stages then (with more, it holds an earlier tile: finite values whose
+  // scores are discarded).  nt is uniform over the workgroup.
+  if (nt < kStages) {
 #pragma unroll
-  for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i) *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
-  tile_barrier();
+    for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i) *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
+    tile_barrier();
+  }
 
   // prefetch the first two tiles while the queries are loaded
   issue_tile(S0{}, 0);

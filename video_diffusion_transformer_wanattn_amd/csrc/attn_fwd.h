@@ -606,7 +606,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     block_step(S, SN, SNN, MASKED, t, 0);
     block_step(S, SN, SNN, MASKED, t, 1);
   };
+  // unrolled over 8 tiles (the loop-carried scores and operands then return
+  // to their registers without the copies a 4-tile body needed), then 4
   int t = 0;
+  for (; t + 8 <= tm; t += 8) {
+    tile_step(S0{}, S1{}, S3{}, NoMask{}, t);
+    tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 1);
+    tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 2);
+    tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 3);
+    tile_step(S0{}, S1{}, S3{}, NoMask{}, t + 4);
+    tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 5);
+    tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 6);
+    tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 7);
+  }
   for (; t + 4 <= tm; t += 4) {
     tile_step(S0{}, S1{}, S3{}, NoMask{}, t);
     tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 1);

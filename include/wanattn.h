@@ -37,7 +37,8 @@
  *    WANATTN_E_INVALID: null or misaligned pointer, sizes < 1, N != F*H*W,
  *    positions reaching 1024, an output overlapping an input, bad lengths.
  *    WANATTN_E_UNSUPPORTED: head_dim != 128, heads > WANATTN_MAX_HEADS, more
- *    distinct theta values than the library keeps tables for.  WANATTN_E_HIP: a HIP call failed.
+ *    distinct theta values than the library keeps tables for, an attention
+ *    launch of more than 2^24 workgroups (min(B, 256) * heads * ceil(N / 256)).  WANATTN_E_HIP: a HIP call failed.
  *    wanattn_last_error() gives a thread-local text for the last failure.
  *  - Calls on different streams may run concurrently.
  */

@@ -91,6 +91,18 @@ def test_workspace_size(lib):
     assert lib.wanattn_self_workspace_bytes(0, 24, 3, 128) == 0
 
 
+def test_launch_size_limit(lib):
+    # 256 batches x 65536 heads x 1 query tile = 2^24 workgroups of 256 threads:
+    # one more thread than a launch takes; rejected before anything is launched
+    g16 = g(1, 16, 16)
+    big = 1 << 44
+    assert lib.wanattn_self(A, B_, C, O, 256, 256, 65536, 128, g16, 1e4, 0.088, 0, 1, None, ctypes.c_void_p(big),
+                            big, None) == wa.E_UNSUPPORTED
+    assert "exceed one launch" in lib.wanattn_last_error().decode()
+    assert lib.wanattn_cross(A, B_, C, O, 256, 256, 8, 65536, 128, 0.088, None, None) == wa.E_UNSUPPORTED
+    assert lib.wanattn_self_kv(A, B_, C, O, 256, 256, 256, 65536, 128, g16, 1e4, 0.088, None, None) == wa.E_UNSUPPORTED
+
+
 def test_self_rejects_positions_beyond_table(lib):
     assert call_self(lib, N=24, grid=g(2, 3, 4, 1023, 0, 0)) == wa.E_INVALID
     assert call_self(lib, N=24, grid=g(2, 3, 4, 0, 1022, 0)) == wa.E_INVALID

@@ -125,6 +125,16 @@ wanattn_status check_tensor_sizes(int32_t B, int32_t N, int32_t heads, int32_t h
   return WANATTN_OK;
 }
 
+// one attention launch covers up to WANATTN_MAX_LEN_BATCH batches x heads x
+// query tiles workgroups of kThreads; a launch takes at most 2^32 - 1 threads
+wanattn_status check_launch_size(int32_t B, int32_t N, int32_t heads) {
+  const long long nb = B < WANATTN_MAX_LEN_BATCH ? B : WANATTN_MAX_LEN_BATCH;
+  const long long wgs = nb * heads * ((N + kBM - 1) / kBM);
+  if (wgs * kThreads > 0xFFFFFFFFll)
+    return fail(WANATTN_E_UNSUPPORTED, "%lld workgroups of %d threads exceed one launch", wgs, kThreads);
+  return WANATTN_OK;
+}
+
 wanattn_status launched(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(WANATTN_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
@@ -220,6 +230,7 @@ wanattn_status check_self(const void* q, const void* k, const void* v, const voi
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
   WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  WA_TRY(check_launch_size(B, N, heads));
   WA_TRY(check_grid(grid, N));
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
   if (mask != WANATTN_MASK_NONE && mask != WANATTN_MASK_BLOCK_CAUSAL)
@@ -321,6 +332,7 @@ wanattn_status check_kv(const void* q, const void* k_cache, const void* v_cache,
     return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
   WA_TRY(check_tensor_sizes(B, Nq, heads, head_dim));
   WA_TRY(check_tensor_sizes(B, Nkv, heads, head_dim));
+  WA_TRY(check_launch_size(B, Nq, heads));
   WA_TRY(check_grid(grid_q, Nq));
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
   const long long hw = (long long)grid_q->H * grid_q->W;
@@ -599,6 +611,7 @@ wanattn_status wanattn_cross(const void* q, const void* k_ctx, const void* v_ctx
   if (!aligned16(q) || !aligned16(k_ctx) || !aligned16(v_ctx) || !aligned16(o))
     return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
   WA_TRY(check_tensor_sizes(B, N, heads, head_dim));
+  WA_TRY(check_launch_size(B, N, heads));
   if (M < 1) return fail(WANATTN_E_INVALID, "M must be >= 1");
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(WANATTN_E_INVALID, "scale must be finite and > 0");
   const size_t qbytes = (size_t)B * N * heads * kHeadDim * 2, cbytes = (size_t)B * M * heads * kHeadDim * 2;

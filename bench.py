@@ -128,6 +128,17 @@ def cpu_baseline(wl, t, threads):
     t_self = a + b * wl.N
     t_cross = tc / len(rc) * wl.N
     f_self, f_cross = flops(wl)
+    # the same on one core, on fewer rows (the key rotation dominates there)
+    s1, s2 = seeded.sample_rows(wl.N, 4, seed=4), seeded.sample_rows(wl.N, 12, seed=5)
+    kw1 = dict(kw, threads=1)
+    u1 = timed(lambda: oracle.self_rows(t["q"], t["k"], t["v"], grid, rows=s1, **kw1))
+    u2 = timed(lambda: oracle.self_rows(t["q"], t["k"], t["v"], grid, rows=s2, **kw1))
+    log(f"cpu oracle, one core: {len(s1)} and {len(s2)} rows x {wl.heads} heads in {u1:.2f}s and {u2:.2f}s")
+    b1 = max((u2 - u1) / (len(s2) - len(s1)), 1e-12)
+    a1 = max(u1 - b1 * len(s1), 0.0)
+    if wl.block_causal:
+        b1 *= b / max((t2 - t1) / (len(rows2) - len(rows1)), 1e-12)   # the same visible-key weighting
+    t_self1 = a1 + b1 * wl.N
     return {
         "value": (f_self + f_cross) / (t_self + t_cross) / 1e12,
         "unit": "TFLOP/s",
@@ -137,7 +148,10 @@ def cpu_baseline(wl, t, threads):
                    f"(self, incl. rotating all keys) and {len(rc)} rows (cross); extrapolated as "
                    f"t = a + b*rows to all {wl.N} rows: self {t_self:.1f} s, cross {t_cross:.1f} s "
                    f"per step"),
-        "cpu_s_measured": t1 + t2 + tc,
+        "cpu_s_measured": t1 + t2 + tc + u1 + u2,
+        "one_core": {"value": f_self / t_self1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                     "sample": (f"self attention only: {len(s1)} and {len(s2)} rows x {wl.heads} heads on one "
+                                f"thread, extrapolated to {t_self1:.0f} s per step")},
     }
 
 

@@ -100,14 +100,22 @@ wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int3
  *   ([P1] ch. 4 seq_lens; ch. 8 pads the sequence to a multiple of the
  *   sequence-parallel size), 1 <= kv_lens[b] <= N.  Every query row is still
  *   written.
- * workspace: caller-owned device memory of at least
- *   wanattn_self_workspace_bytes(B, N, heads, head_dim) bytes, 16-byte
- *   aligned, not overlapping q, k, v or o.  It receives the rotated keys k'
- *   (one rotation per key, shared by every query tile); its contents after the
- *   call are unspecified.  Calls that may run concurrently need separate
- *   workspaces.
+ * workspace: caller-owned device memory, 16-byte aligned, not overlapping q,
+ *   k, v or o, of at least B*N*heads*head_dim*2 bytes: it receives the
+ *   rotated keys k' (one rotation per key, shared by every query tile).
+ *   wanattn_self_workspace_bytes(B, N, heads, head_dim) adds room for fp32
+ *   partial results (at most 512 * 130 KiB): with it, when the bidirectional
+ *   launch's last wave of workgroups would fill at most half the chip, those
+ *   query tiles run as several workgroups each over ranges of the keys, whose
+ *   partial softmax results a second kernel combines.  A smaller workspace
+ *   runs without that split.  The contents after the call are unspecified.
+ *   Calls that may run concurrently need separate workspaces.
  * Accumulation is fp32; the MFMA operands (rotated and scaled q, rotated k,
  * softmax probabilities, v) are bf16; o is rounded to bf16 (nearest even).
+ * Rows of split tiles are combined in a different order, so they can differ
+ * from an unsplit run in the last bit; which tiles split depends on the
+ * device's compute-unit count.  Repeated calls on one device give identical
+ * bits.
  */
 wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o, int32_t B,
                             int32_t N, int32_t heads, int32_t head_dim,
@@ -115,7 +123,8 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
                             wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* bytes of workspace wanattn_self needs for these sizes (0 for invalid sizes) */
+/* bytes of workspace for wanattn_self with these sizes, the split's room
+ * included (0 for invalid sizes) */
 size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim);
 
 #define WANATTN_MAX_JITTER_HEADS 256
@@ -129,11 +138,13 @@ size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t
  * values, e.g. theta * (1 + eps_h)).  Equal values reproduce wanattn_self.
  * theta_per_head: HOST array [heads], each finite and > 0; heads <=
  *   WANATTN_MAX_JITTER_HEADS (else WANATTN_E_UNSUPPORTED).
- * workspace: at least wanattn_self_jitter_workspace_bytes(...) bytes, 16-byte
- *   aligned, not overlapping q, k, v or o.  It receives the per-head rotary
- *   tables (built on the device in fp64 and rounded to fp32 on every call,
- *   768 KiB per head) followed by the rotated keys.  Everything else, including
- *   errors and numerics, is as wanattn_self.
+ * workspace: 16-byte aligned, not overlapping q, k, v or o, of at least
+ *   heads * 768 KiB + B*N*heads*head_dim*2 bytes.  It receives the per-head
+ *   rotary tables (built on the device in fp64 and rounded to fp32 on every
+ *   call, 768 KiB per head) followed by the rotated keys;
+ *   wanattn_self_jitter_workspace_bytes(...) adds the room for the tail
+ *   split's partials as in wanattn_self.  Everything else, including errors
+ *   and numerics, is as wanattn_self.
  */
 wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, void* o, int32_t B,
                                    int32_t N, int32_t heads, int32_t head_dim,
@@ -141,7 +152,8 @@ wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, 
                                    wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* bytes of workspace wanattn_self_jitter needs (0 for invalid sizes) */
+/* bytes of workspace for wanattn_self_jitter, the split's room included (0
+ * for invalid sizes) */
 size_t wanattn_self_jitter_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim);
 
 /*

@@ -52,3 +52,21 @@ def assert_parity(got_bits, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS, rel_rms=REL
     assert e["mean_abs"] <= mean_abs, msg
     assert e["rel_rms"] <= rel_rms, msg
     return e
+
+
+def split_heads(B, N, heads, n_cu):
+    """(batch, head) pairs holding the query tiles that bidirectional self
+    attention runs as key-split workgroups on a chip of n_cu compute units
+    (with a workspace that has room for the partials): a remainder of at most
+    half the chip, or the last whole wave of 4 or more."""
+    ntq = (N + 255) // 256
+    total = B * heads * ntq
+    rem = total % n_cu
+    if rem == 0 and total >= 4 * n_cu:
+        tail = n_cu
+    elif rem and total > n_cu and 2 * rem <= n_cu:
+        tail = rem
+    else:
+        tail = 0
+    bhs = sorted({L // ntq for L in range(total - tail, total)})
+    return [(bh // heads, bh % heads) for bh in bhs]

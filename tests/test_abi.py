@@ -85,10 +85,28 @@ def test_self_rejects(lib, kw, status):
     assert lib.wanattn_last_error()
 
 
+# room for the fp32 partials of one key-split workgroup: 256 rows x 128 O
+# values and (l, bias) per row
+SPLIT_ITEM = 256 * 128 * 4 + 256 * 8
+
+
 def test_workspace_size(lib):
-    assert lib.wanattn_self_workspace_bytes(2, 24, 3, 128) == 2 * 24 * 3 * 128 * 2
+    # rotated keys, plus partials for as many split workgroups as the launch
+    # has workgroups (at most 512)
+    assert lib.wanattn_self_workspace_bytes(2, 24, 3, 128) == 2 * 24 * 3 * 128 * 2 + 6 * SPLIT_ITEM
+    assert lib.wanattn_self_workspace_bytes(1, 75600, 40, 128) == 75600 * 40 * 128 * 2 + 512 * SPLIT_ITEM
     assert lib.wanattn_self_workspace_bytes(2, 24, 3, 64) == 0
     assert lib.wanattn_self_workspace_bytes(0, 24, 3, 128) == 0
+
+
+def test_workspace_room_for_partials_is_checked_for_overlap(lib):
+    # the rotated keys' part of the workspace ends before k, the partials'
+    # room does not: rejected when the caller offers that room
+    kbytes = 24 * 2 * 128 * 2
+    full = lib.wanattn_self_workspace_bytes(1, 24, 2, 128)
+    ws = ctypes.c_void_p((2 << 30) - kbytes - 256)
+    assert call_self(lib, ws=ws, ws_bytes=full) == wa.E_INVALID
+    assert "overlaps" in lib.wanattn_last_error().decode()
 
 
 def test_launch_size_limit(lib):
@@ -168,7 +186,7 @@ def test_rope3d_rejects(lib):
 
 def test_self_jitter_workspace_and_rejects(lib):
     tab = 3 * 1024 * 32 * 8                       # one head's rotary table
-    assert lib.wanattn_self_jitter_workspace_bytes(2, 24, 3, 128) == 3 * tab + 2 * 24 * 3 * 128 * 2
+    assert lib.wanattn_self_jitter_workspace_bytes(2, 24, 3, 128) == 3 * tab + 2 * 24 * 3 * 128 * 2 + 6 * SPLIT_ITEM
     assert lib.wanattn_self_jitter_workspace_bytes(1, 24, 257, 128) == 0
     assert lib.wanattn_self_jitter_workspace_bytes(1, 24, 3, 64) == 0
     th3 = (ctypes.c_double * 3)(1e4, 5e2, 2e5)

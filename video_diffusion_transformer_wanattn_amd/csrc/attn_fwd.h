@@ -81,8 +81,23 @@ struct AttnParams {
   int H, W, f0, h0, w0;
   double inv_hw, inv_w;
   int chunk_tokens;   // block-causal chunk length in tokens
+  // key-split tail (SPLIT kernels only): workgroups total.. run the query tiles
+  // total, total + 1, .. (in the tile order above) as nsplit workgroups each,
+  // over consecutive ranges of key tiles, writing partial results to part_o
+  // and part_lb instead of O (see split_merge_kernel)
+  float4* part_o;
+  float2* part_lb;
+  int nsplit;
   int lens[WANATTN_MAX_LEN_BATCH];  // visible keys per batch (1..Nk)
 };
+
+// Partial results of one split workgroup, in the order its lanes hold them:
+// O (not normalised) as kBM * kHeadDim / 4 float4, index
+// ((2 * wave + qb) * 16 + 4 * db + g4) * 64 + lane for query row
+// 64 wave + 32 qb + (lane & 31) and d = 32 db + 8 g4 + 4 (lane >> 5) + 0..3;
+// the row sum l and the bias b (minus the reference O and l are taken
+// against) as kBM float2, index (2 * wave + qb) * 32 + row % 32.
+constexpr int kPartO = kBM * kHeadDim / 4;
 
 // K row slot of physical key t inside a tile: swap bits 2 and 3 (an involution)
 __device__ __forceinline__ int k_slot(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
@@ -138,8 +153,9 @@ __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
-template <bool ROPE, bool CAUSAL>
+template <bool ROPE, bool CAUSAL, bool SPLIT = false>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
+  static_assert(!(SPLIT && CAUSAL), "key splits are built for the bidirectional mask");
   // LDS: the K' halves of the 4 stages in the first 64 KiB, their V halves in
   // the second, so that every operand read is one base register (per lane)
   // plus an immediate offset below 64 KiB (the ds_read offset field)
@@ -158,9 +174,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // ---- workgroup -> (batch, head, query tile).  Workgroup w runs on XCD w % 8;
   // give each XCD a contiguous run of tiles so that the concurrent workgroups of
   // an XCD walk the same head's K/V through their shared L2.
+  // Key-split workgroups (total and above) take split ks of tile total + item / nsplit.
   const int wg = blockIdx.x;
-  const int per = p.total >> 3, rem = p.total & 7, x = wg & 7;
-  const int L = x * per + (x < rem ? x : rem) + (wg >> 3);
+  const bool split = SPLIT && wg >= p.total;
+  const int item = wg - p.total;
+  int L, ks = 0;
+  if (split) {
+    L = p.total + item / p.nsplit;
+    ks = item - (item / p.nsplit) * p.nsplit;
+  } else {
+    const int per = p.total >> 3, rem = p.total & 7, x = wg & 7;
+    L = x * per + (x < rem ? x : rem) + (wg >> 3);
+  }
   const int bh = L / p.ntq;
   int tq = L - bh * p.ntq;
   if (CAUSAL) tq = p.ntq - 1 - tq;  // heaviest tiles of a head first
@@ -170,7 +195,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, hh = lane >> 5;
-  const int kvl = p.lens[b];
+  // keys [k0, k0 + Nk) of the batch are this workgroup's (all of them unless split)
+  int k0 = 0, Nk = p.Nk, kvl = p.lens[b];
+  if (split) {
+    // the host launches splits only where every range holds a key
+    const int nkt = (kvl + kBN - 1) / kBN;
+    const int t_lo = ks * nkt / p.nsplit, t_hi = (ks + 1) * nkt / p.nsplit;
+    k0 = t_lo * kBN;
+    Nk = min(t_hi * kBN, kvl) - k0;
+    kvl = Nk;
+  }
   const int i_last = min(i0 + kBM, p.N) - 1;
   const int kv_end = row_limit<CAUSAL>(p, kvl, i_last);
   const int kv_full = row_limit<CAUSAL>(p, kvl, i0);
@@ -180,8 +214,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   const size_t row_stride = (size_t)p.heads * kHeadDim;  // elements between tokens
   const uint32_t rsb = (uint32_t)(row_stride * 2);        // bytes between tokens
   const uint16_t* qbase = p.q + ((size_t)b * p.N * p.heads + head) * kHeadDim;
-  const char* kbase = (const char*)(p.k + ((size_t)b * p.Nk * p.heads + head) * kHeadDim);
-  const char* vbase = (const char*)(p.v + ((size_t)b * p.Nk * p.heads + head) * kHeadDim);
+  const char* kbase = (const char*)(p.k + (((size_t)b * p.Nk + k0) * p.heads + head) * kHeadDim);
+  const char* vbase = (const char*)(p.v + (((size_t)b * p.Nk + k0) * p.heads + head) * kHeadDim);
 
   // ---- tile loads straight into LDS.  Instruction i of wave w fills 1 KiB:
   // rows m = 16w + 4i + l/16 (l = lane), stored chunk l%16 holding global chunk
@@ -223,15 +257,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
     const char* kt = kbase + (size_t)t * kBN * rsb;
     const char* vt = vbase + (size_t)t * kBN * rsb;
-    if (t * kBN + kBN <= p.Nk) {
+    if (t * kBN + kBN <= Nk) {
       issue_full_tile(S, t);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int blk = 4 * wave + i;
         const int m = 4 * blk + ld_row;
-        const int kkey = min(t * kBN + k_slot(m), p.Nk - 1) - t * kBN;
-        const int vkey = min(t * kBN + m, p.Nk - 1) - t * kBN;
+        const int kkey = min(t * kBN + k_slot(m), Nk - 1) - t * kBN;
+        const int vkey = min(t * kBN + m, Nk - 1) - t * kBN;
         dma16(kt, (uint32_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m)), st + blk * 1024);
         dma16(vt, (uint32_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m)), st + kVHalves + blk * 1024);
       }
@@ -601,7 +635,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   // unrolled loop with compile-time stages; the rest (the last few tiles, or
   // the chunk a causal query tile straddles) run in a loop with run-time stages.
   const int jm = kv_full / 32;
-  const int tm = max(0, min(min(nt, (jm - 1) / 2), p.Nk / kBN - 3));
+  const int tm = max(0, min(min(nt, (jm - 1) / 2), Nk / kBN - 3));
   auto tile_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t) __attribute__((always_inline)) {
     block_step(S, SN, SNN, MASKED, t, 0);
     block_step(S, SN, SNN, MASKED, t, 1);
@@ -626,6 +660,27 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 3);
   }
   for (; t < nt; ++t) tile_step(t, t + 1, t + 3, Mask{}, t);
+
+  if (split) {
+    // ---- partial epilogue: O, l and the bias as they stand, fp32, one
+    // whole 1 KiB run of float4 per store instruction
+    acc_fence();
+    float4* po = p.part_o + (size_t)item * kPartO + (size_t)(2 * wave) * 16 * 64 + lane;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l = wave_half_sum(lrun[qb]);
+      if (hh == 0) p.part_lb[(size_t)item * kBM + (2 * wave + qb) * 32 + r] = make_float2(l, bias[qb]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          po[(qb * 16 + 4 * db + g4) * 64] =
+              make_float4(acc[qb][db][4 * g4 + 0], acc[qb][db][4 * g4 + 1], acc[qb][db][4 * g4 + 2],
+                          acc[qb][db][4 * g4 + 3]);
+    }
+    wait_vm<0>();
+    return;
+  }
 
   // ---- epilogue: O = O^T / l, bf16.  A lane holds d = 32 db + 8 g4 + 4 hh + 0..3
   // of one query; each wave writes its 64 rows into LDS (chunks XOR-swizzled
@@ -660,6 +715,56 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     const u32x4 w = *(const u32x4*)(orows + row * kRowBytes + 16 * (sc ^ (row & 15)));
     if (irow0 + 4 * it < p.N) *(u32x4*)dst = w;
     dst += 4 * row_stride;
+  }
+}
+
+// ---- the key splits of the tail tiles combined.  Split s holds O_s and l_s
+// against its own reference m_s = -b_s; with M = max_s m_s the row is
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s (the same rescaling the
+// streaming softmax applies when its reference moves).  Workgroup: one
+// (tile, 32-row block) of a tail tile; thread: 4 consecutive d of a row, in
+// the partials' own order, so that every read is a whole 1 KiB run.
+struct MergeParams {
+  const float4* part_o;
+  const float2* part_lb;
+  uint16_t* o;
+  int first;   // tile index (in the attention kernel's order) of the first tail tile
+  int ntq, heads, N, nsplit;
+};
+
+__global__ void __launch_bounds__(256) split_merge_kernel(MergeParams p) {
+  const int tile = blockIdx.x >> 3, blk = blockIdx.x & 7;  // blk = 2 wave + qb
+  const int L = p.first + tile;
+  const int bh = L / p.ntq, tq = L - bh * p.ntq;
+  const int b = bh / p.heads, head = bh - b * p.heads;
+  const int item0 = tile * p.nsplit;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = threadIdx.x + 256 * k;  // (4 db + g4) * 64 + lane
+    const int lane = c & 63, dg = c >> 6, r = lane & 31, hh = lane >> 5;
+    const int row = tq * kBM + 32 * blk + r;
+    float m = -__builtin_inff();
+    for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, -p.part_lb[(size_t)(item0 + s) * kBM + 32 * blk + r].y);
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float l = 0.0f;
+    for (int s = 0; s < p.nsplit; ++s) {
+      const float2 lb = p.part_lb[(size_t)(item0 + s) * kBM + 32 * blk + r];
+      const float w = __builtin_amdgcn_exp2f(-lb.y - m);
+      const float4 os = p.part_o[(size_t)(item0 + s) * kPartO + (16 * blk + dg) * 64 + lane];
+      l += w * lb.x;
+      o.x += w * os.x;
+      o.y += w * os.y;
+      o.z += w * os.z;
+      o.w += w * os.w;
+    }
+    const float inv = 1.0f / l;
+    if (row < p.N) {
+      u32x2 wd;
+      wd[0] = pack_bf16x2(o.x * inv, o.y * inv);
+      wd[1] = pack_bf16x2(o.z * inv, o.w * inv);
+      const int d = 32 * (dg >> 2) + 8 * (dg & 3) + 4 * hh;
+      *(u32x2*)(p.o + ((size_t)b * p.N + row) * ((size_t)p.heads * kHeadDim) + (size_t)head * kHeadDim + d) = wd;
+    }
   }
 }
 

@@ -155,10 +155,63 @@ wanattn_status check_lens(int32_t B, const int32_t* lens, int32_t maxlen, const 
   return WANATTN_OK;
 }
 
+// Tail splitting of bidirectional self attention.  A launch of T workgroups on
+// a chip of C compute units runs floor(T / C) full waves of workgroups and then
+// T % C alone, which leaves most of the chip idle for a whole workgroup's time;
+// and the workgroups of the last full wave end over a spread of times (they
+// started over one), during which the chip empties.  The last query tiles run
+// instead as nsplit workgroups each, every one over a range of the key tiles,
+// writing fp32 partials into the caller's workspace; a small kernel then
+// combines them.  The short workgroups fill the chip as it empties:
+//  - a remainder of at most C / 2 tiles: nsplit = C / remainder (at most 8);
+//  - no remainder, at least 4 waves: the last wave, nsplit = 2.
+// (Measured on the 75,600- and 32,760-token workloads, 40 heads: 4 to 5% and
+// 2 to 3.5% shorter; finer splits or more split tiles gained nothing more.)
+// kSplitItemBytes per split workgroup.
+constexpr int kMaxSplit = 8;
+constexpr int kMaxSplitItems = 512;
+constexpr size_t kSplitItemBytes = (size_t)kPartO * sizeof(float4) + (size_t)kBM * sizeof(float2);
+
+// split workgroups a self-attention call can use (its workspace holds that many)
+size_t split_items(int32_t B, int32_t N, int32_t heads) {
+  const long long nb = B < WANATTN_MAX_LEN_BATCH ? B : WANATTN_MAX_LEN_BATCH;
+  const long long wgs = nb * heads * ((N + kBM - 1) / kBM);
+  return (size_t)(wgs < kMaxSplitItems ? wgs : kMaxSplitItems);
+}
+
+// the split (0: none) for a launch of `total` workgroups whose shortest
+// visible key range is minlen, with room for `room` split workgroups
+int choose_split(int total, int minlen, size_t room, int* tail_out) {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 2)
+    return 0;
+  const int rem = total % ncu;
+  int tail, nsplit;
+  if (rem == 0 && total >= 4 * ncu) {
+    tail = ncu;
+    nsplit = 2;
+  } else if (rem > 0 && total > ncu && 2 * rem <= ncu) {
+    tail = rem;
+    nsplit = ncu / rem < kMaxSplit ? ncu / rem : kMaxSplit;
+  } else {
+    return 0;
+  }
+  // at least 8 key tiles per range: shorter ones gain less than they cost
+  const int nkt = (minlen + kBN - 1) / kBN;
+  while (nsplit > 1 && nkt < 8 * nsplit) --nsplit;
+  while (nsplit > 1 && (size_t)tail * nsplit > room) --nsplit;
+  if (nsplit < 2 || ((long long)total - tail + (long long)tail * nsplit) * kThreads > 0xFFFFFFFFll) return 0;
+  *tail_out = tail;
+  return nsplit;
+}
+
 // Launch over groups of at most WANATTN_MAX_LEN_BATCH batches so that the
-// per-batch key lengths always fit the kernel argument block.
+// per-batch key lengths always fit the kernel argument block.  `part` (room
+// for part_items split workgroups, or null) enables tail splitting.
 template <bool ROPE, bool CAUSAL>
-wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStream_t stream) {
+wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStream_t stream,
+                           void* part = nullptr, size_t part_items = 0) {
   const size_t qstride = (size_t)p.N * p.heads * kHeadDim, kstride = (size_t)p.Nk * p.heads * kHeadDim;
   const uint16_t *q0 = p.q, *k0 = p.k, *v0 = p.v;
   uint16_t* o0 = p.o;
@@ -171,6 +224,24 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
     p.o = o0 + (size_t)b0 * qstride;
     for (int b = 0; b < nb; ++b) p.lens[b] = lens ? lens[b0 + b] : p.Nk;
     p.total = nb * p.heads * p.ntq;
+    if constexpr (ROPE && !CAUSAL) {
+      int minlen = p.Nk, tail = 0;
+      for (int b = 0; b < nb; ++b) minlen = p.lens[b] < minlen ? p.lens[b] : minlen;
+      const int nsplit = part ? choose_split(p.total, minlen, part_items, &tail) : 0;
+      if (nsplit) {
+        p.total -= tail;
+        p.nsplit = nsplit;
+        p.part_o = (float4*)part;
+        p.part_lb = (float2*)((char*)part + part_items * kPartO * sizeof(float4));
+        hipLaunchKernelGGL((attn_fwd_kernel<ROPE, false, true>), dim3(p.total + tail * nsplit), dim3(kThreads), 0,
+                           stream, p);
+        WA_TRY(launched("attention"));
+        MergeParams m{p.part_o, p.part_lb, p.o, p.total, p.ntq, p.heads, p.N, nsplit};
+        hipLaunchKernelGGL(split_merge_kernel, dim3(tail * 8), dim3(256), 0, stream, m);
+        WA_TRY(launched("split merge"));
+        continue;
+      }
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<ROPE, CAUSAL>), dim3(p.total), dim3(kThreads), 0, stream, p);
     WA_TRY(launched("attention"));
   }
@@ -221,11 +292,12 @@ wanattn_status rope3d_checked(const void* x, void* y, int32_t B, int32_t N, int3
 }
 
 // argument checks shared by the self-attention entry points (theta checked by
-// the caller); the workspace must hold ws_need bytes
+// the caller); the workspace must hold ws_need bytes, of which the call uses
+// ws_use (ws_need, or more where the tail split's partials fit)
 wanattn_status check_self(const void* q, const void* k, const void* v, const void* o, int32_t B, int32_t N,
                           int32_t heads, int32_t head_dim, const wanattn_grid3d* grid, float scale,
                           wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
-                          const void* workspace, size_t workspace_bytes, size_t ws_need) {
+                          const void* workspace, size_t workspace_bytes, size_t ws_need, size_t ws_use) {
   if (!q || !k || !v || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
@@ -244,8 +316,8 @@ wanattn_status check_self(const void* q, const void* k, const void* v, const voi
   if (!aligned16(workspace)) return fail(WANATTN_E_INVALID, "workspace must be 16-byte aligned");
   if (workspace_bytes < ws_need)
     return fail(WANATTN_E_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, ws_need);
-  if (overlap(workspace, ws_need, q, bytes) || overlap(workspace, ws_need, k, bytes) ||
-      overlap(workspace, ws_need, v, bytes) || overlap(workspace, ws_need, o, bytes))
+  if (overlap(workspace, ws_use, q, bytes) || overlap(workspace, ws_use, k, bytes) ||
+      overlap(workspace, ws_use, v, bytes) || overlap(workspace, ws_use, o, bytes))
     return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
   return check_lens(B, kv_lens, N, "kv_lens");
 }
@@ -255,7 +327,7 @@ wanattn_status check_self(const void* q, const void* k, const void* v, const voi
 wanattn_status self_launch(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t N,
                            int32_t heads, const wanattn_grid3d* grid, float scale, wanattn_mask mask,
                            int32_t chunk_frames, const int32_t* kv_lens, void* kprime, const float2* tab,
-                           long long hstride, hipStream_t stream) {
+                           long long hstride, void* part, size_t part_items, hipStream_t stream) {
   WA_TRY(rope3d_launch(k, kprime, B, N, heads, grid, tab, hstride, stream));
   AttnParams p;
   memset(&p, 0, sizeof p);
@@ -281,7 +353,7 @@ wanattn_status self_launch(const void* q, const void* k, const void* v, void* o,
     p.chunk_tokens = (int)(ct < N ? ct : N);
     return launch_attn<true, true>(p, B, kv_lens, stream);
   }
-  return launch_attn<true, false>(p, B, kv_lens, stream);
+  return launch_attn<true, false>(p, B, kv_lens, stream, part, part_items);
 }
 
 size_t jitter_table_bytes(int heads) { return (size_t)heads * kTabEntries * sizeof(float2); }
@@ -508,7 +580,7 @@ wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int3
 
 size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim) {
   if (B < 1 || N < 1 || heads < 1 || head_dim != kHeadDim) return 0;
-  return (size_t)B * N * heads * kHeadDim * 2;
+  return (size_t)B * N * heads * kHeadDim * 2 + split_items(B, N, heads) * kSplitItemBytes;
 }
 
 wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o, int32_t B,
@@ -519,17 +591,19 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
   t_err[0] = 0;
   WA_TRY(check_theta(theta));
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  const size_t items = split_items(B, N, heads), full = bytes + items * kSplitItemBytes;
+  const bool room = workspace_bytes >= full;
   WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
-                    workspace_bytes, bytes));
+                    workspace_bytes, bytes, room ? full : bytes));
   const float2* tab = nullptr;
   WA_TRY(table_for(theta, &tab));
   return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens, workspace, tab, 0,
-                     (hipStream_t)stream);
+                     room ? (char*)workspace + bytes : nullptr, room ? items : 0, (hipStream_t)stream);
 }
 
 size_t wanattn_self_jitter_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim) {
   if (B < 1 || N < 1 || heads < 1 || heads > kMaxJitterHeads || head_dim != kHeadDim) return 0;
-  return jitter_table_bytes(heads) + (size_t)B * N * heads * kHeadDim * 2;
+  return jitter_table_bytes(heads) + (size_t)B * N * heads * kHeadDim * 2 + split_items(B, N, heads) * kSplitItemBytes;
 }
 
 wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, void* o, int32_t B,
@@ -542,11 +616,14 @@ wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, 
   WA_TRY(check_head_thetas(theta_per_head, heads));
   const size_t tbytes = jitter_table_bytes(heads);
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  const size_t items = split_items(B, N, heads), full = tbytes + bytes + items * kSplitItemBytes;
+  const bool room = workspace_bytes >= full;
   WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
-                    workspace_bytes, tbytes + bytes));
+                    workspace_bytes, tbytes + bytes, room ? full : tbytes + bytes));
   WA_TRY(build_head_tables(theta_per_head, heads, (float2*)workspace, (hipStream_t)stream));
   return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens,
-                     (char*)workspace + tbytes, (const float2*)workspace, kTabEntries, (hipStream_t)stream);
+                     (char*)workspace + tbytes, (const float2*)workspace, kTabEntries,
+                     room ? (char*)workspace + tbytes + bytes : nullptr, room ? items : 0, (hipStream_t)stream);
 }
 
 wanattn_status wanattn_self_kv(const void* q, const void* k_cache, const void* v_cache, void* o,

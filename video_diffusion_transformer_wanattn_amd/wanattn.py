@@ -200,8 +200,10 @@ def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = 
     theta_per_head: optional [heads] RoPE bases (multi-head RoPE jitter; theta
     is then unused).  workspace: optional GPU tensor of at least
     self_workspace_bytes(...) bytes (self_jitter_workspace_bytes(...) with
-    theta_per_head); the rotated keys (and per-head tables) go there; allocated
-    per call when not given."""
+    theta_per_head); the rotated keys (and per-head tables) go there, and the
+    partial results of the key-split tail where it has room for them (a
+    workspace of just the rotated keys' size runs without that split);
+    allocated per call when not given."""
     import torch
     lib = load_library()
     if out is None:

@@ -370,12 +370,14 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    # rotated keys and the key-split partials, allocated once
+    ws = torch.empty(wa.self_workspace_bytes(wl.batch, wl.N, wl.heads), dtype=torch.uint8, device="cuda")
 
     def step(events=None):
         if events is not None:
             events[0].record(stream)
         wa.self_attention(q, k, v, grid, block_causal=wl.block_causal, chunk_frames=wl.chunk_frames,
-                          out=o_self)
+                          out=o_self, workspace=ws)
         if events is not None:
             events[1].record(stream)
         wa.cross_attention(q, kc, vc, out=o_cross)

@@ -86,15 +86,16 @@ def test_self_rejects(lib, kw, status):
 
 
 # room for the fp32 partials of one key-split workgroup: 256 rows x 128 O
-# values and (l, bias) per row
+# values and (l, bias) per row; then 256 bytes of work-queue counters
 SPLIT_ITEM = 256 * 128 * 4 + 256 * 8
+QUEUE = 256
 
 
 def test_workspace_size(lib):
     # rotated keys, plus partials for as many split workgroups as the launch
-    # has workgroups (at most 512)
-    assert lib.wanattn_self_workspace_bytes(2, 24, 3, 128) == 2 * 24 * 3 * 128 * 2 + 6 * SPLIT_ITEM
-    assert lib.wanattn_self_workspace_bytes(1, 75600, 40, 128) == 75600 * 40 * 128 * 2 + 512 * SPLIT_ITEM
+    # has workgroups (at most 512), plus the queue counters
+    assert lib.wanattn_self_workspace_bytes(2, 24, 3, 128) == 2 * 24 * 3 * 128 * 2 + 6 * SPLIT_ITEM + QUEUE
+    assert lib.wanattn_self_workspace_bytes(1, 75600, 40, 128) == 75600 * 40 * 128 * 2 + 512 * SPLIT_ITEM + QUEUE
     assert lib.wanattn_self_workspace_bytes(2, 24, 3, 64) == 0
     assert lib.wanattn_self_workspace_bytes(0, 24, 3, 128) == 0
 
@@ -186,7 +187,8 @@ def test_rope3d_rejects(lib):
 
 def test_self_jitter_workspace_and_rejects(lib):
     tab = 3 * 1024 * 32 * 8                       # one head's rotary table
-    assert lib.wanattn_self_jitter_workspace_bytes(2, 24, 3, 128) == 3 * tab + 2 * 24 * 3 * 128 * 2 + 6 * SPLIT_ITEM
+    assert lib.wanattn_self_jitter_workspace_bytes(2, 24, 3, 128) == (3 * tab + 2 * 24 * 3 * 128 * 2 + 6 * SPLIT_ITEM
+                                                                      + QUEUE)
     assert lib.wanattn_self_jitter_workspace_bytes(1, 24, 257, 128) == 0
     assert lib.wanattn_self_jitter_workspace_bytes(1, 24, 3, 64) == 0
     th3 = (ctypes.c_double * 3)(1e4, 5e2, 2e5)

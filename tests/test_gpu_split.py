@@ -128,3 +128,16 @@ def test_workspace_without_room_turns_the_split_off():
     # outside the split tiles both calls run the same workgroups: identical bits
     other = np.setdiff1d(np.arange(heads), hs)
     assert np.array_equal(got_small[:, :, other], got_full[:, :, other])
+
+
+@pytest.mark.parametrize("name", ["wan14b_720p_81f", "wan14b_480p_81f"])
+def test_every_tile_written_at_full_size(name):
+    # the persistent launch hands out every query tile exactly once through
+    # its work queues: an output filled with NaN beforehand has none left
+    wl = seeded.WORKLOADS[name]
+    t = seeded.workload_tensors(wl, seed=0, cross=False)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    o = torch.full_like(q, float("nan"))
+    wa.self_attention(q, k, v, (wl.F, wl.H, wl.W), theta=THETA, out=o)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())

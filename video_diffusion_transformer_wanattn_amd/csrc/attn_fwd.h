@@ -81,15 +81,21 @@ struct AttnParams {
   int H, W, f0, h0, w0;
   double inv_hw, inv_w;
   int chunk_tokens;   // block-causal chunk length in tokens
-  // key-split tail (SPLIT kernels only): workgroups total.. run the query tiles
-  // total, total + 1, .. (in the tile order above) as nsplit workgroups each,
-  // over consecutive ranges of key tiles, writing partial results to part_o
-  // and part_lb instead of O (see split_merge_kernel)
+  // Persistent launches (PERSIST kernels): one workgroup per compute unit
+  // takes work items from queue (9 counters, zero at launch): the query tiles
+  // 0 .. total-1, split into 8 contiguous runs, one per XCD (own run first,
+  // then the other runs), and then the split items 0 .. nsplit_items-1 of the
+  // key-split tail: item s runs key range s % nsplit of query tile
+  // total + s / nsplit, writing partial results to part_o and part_lb instead
+  // of O (see split_merge_kernel)
+  unsigned* queue;
   float4* part_o;
   float2* part_lb;
-  int nsplit;
+  int nsplit, nsplit_items;
   int lens[WANATTN_MAX_LEN_BATCH];  // visible keys per batch (1..Nk)
 };
+
+constexpr int kQueueCounters = 9;  // one per XCD, then the split items
 
 // Partial results of one split workgroup, in the order its lanes hold them:
 // O (not normalised) as kBM * kHeadDim / 4 float4, index
@@ -105,8 +111,9 @@ __device__ __forceinline__ int k_slot(int t) { return (t & ~12) | ((t & 4) << 1)
 __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 __device__ __forceinline__ int v_swz(int row) { return 4 * (row & 3); }
 
-template <bool CAUSAL>
-__device__ __forceinline__ int row_limit(const AttnParams& p, int kvl, int i) {
+// (P: the argument block, in whichever address space the kernel reads it from)
+template <bool CAUSAL, class P>
+__device__ __forceinline__ int row_limit(const P& p, int kvl, int i) {
   int lim = kvl;
   if (CAUSAL) {
     int ce = (i / p.chunk_tokens + 1) * p.chunk_tokens;
@@ -131,6 +138,23 @@ __device__ __forceinline__ uint32_t rotate_pair(uint32_t w, const float2* tab, i
   return pack_bf16x2(re * scale, im * scale);
 }
 
+// Next work item of a persistent workgroup on XCD x (one lane calls this):
+// a query tile from XCD x's run, else from the runs of XCDs x+1, x+2, .. (k
+// is the caller's cursor over them), else a split item (returned as total +
+// s), else -1.  Counters only grow; a draw past the end of a run is unused.
+__device__ __forceinline__ int next_item(const AttnParams& p, int x, int& k) {
+  const int per = p.total >> 3, rem = p.total & 7;
+  while (k < 8) {
+    const int y = (x + k) & 7;
+    const int n = per + (y < rem ? 1 : 0);
+    const unsigned j = __hip_atomic_fetch_add(p.queue + y, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (j < (unsigned)n) return y * per + (y < rem ? y : rem) + (int)j;
+    ++k;
+  }
+  const unsigned s = __hip_atomic_fetch_add(p.queue + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return s < (unsigned)p.nsplit_items ? p.total + (int)s : -1;
+}
+
 // wait until at most n of this wave's vector-memory operations are outstanding
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -153,9 +177,9 @@ __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
-template <bool ROPE, bool CAUSAL, bool SPLIT = false>
-__global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
-  static_assert(!(SPLIT && CAUSAL), "key splits are built for the bidirectional mask");
+template <bool ROPE, bool CAUSAL, bool PERSIST = false>
+__global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg) {
+  static_assert(!(PERSIST && CAUSAL), "persistent launches are built for the bidirectional mask");
   // LDS: the K' halves of the 4 stages in the first 64 KiB, their V halves in
   // the second, so that every operand read is one base register (per lane)
   // plus an immediate offset below 64 KiB (the ds_read offset field)
@@ -171,18 +195,52 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
 
-  // ---- workgroup -> (batch, head, query tile).  Workgroup w runs on XCD w % 8;
-  // give each XCD a contiguous run of tiles so that the concurrent workgroups of
-  // an XCD walk the same head's K/V through their shared L2.
-  // Key-split workgroups (total and above) take split ks of tile total + item / nsplit.
-  const int wg = blockIdx.x;
-  const bool split = SPLIT && wg >= p.total;
-  const int item = wg - p.total;
-  int L, ks = 0;
-  if (split) {
-    L = p.total + item / p.nsplit;
-    ks = item - (item / p.nsplit) * p.nsplit;
+  __shared__ int s_item;
+  int cursor = 0;  // lane 0 of wave 0: the queue it draws from (next_item)
+  const int xcc = PERSIST ? (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7) : 0;  // HW_REG_XCC_ID
+
+  // one work item per pass; a plain launch makes one pass
+  for (;;) {
+  // A persistent pass reads the arguments again from the kernel argument
+  // segment (through a pointer the compiler cannot see through) and derives
+  // the lane constants again: otherwise they are all kept in registers across
+  // passes (~100 SGPRs and ~80 VGPRs of spills).
+  const auto& p = [&]() -> decltype(auto) {
+    if constexpr (PERSIST) {
+      auto kp = (const __attribute__((address_space(4))) AttnParams*)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(kp));
+      return *kp;
+    } else {
+      return (const AttnParams&)p_arg;
+    }
+  }();
+  int tid = threadIdx.x;
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 31, hh = lane >> 5;
+  // ---- work item -> (batch, head, query tile).  A plain launch runs workgroup w
+  // on XCD w % 8; it gives each XCD a contiguous run of tiles so that the
+  // concurrent workgroups of an XCD walk the same head's K/V through their
+  // shared L2.  A persistent launch keeps those runs as the XCDs' queues.
+  // A split item takes key range ks of tile total + item / nsplit.
+  int L, ks = 0, item = 0;
+  bool split = false;
+  if constexpr (PERSIST) {
+    // every thread has read the previous item (its pass had barriers since)
+    if (tid == 0) s_item = next_item(p_arg, xcc, cursor);
+    __syncthreads();
+    const int it = s_item;
+    if (it < 0) break;
+    split = it >= p.total;
+    L = it;
+    if (split) {
+      item = it - p.total;
+      L = p.total + item / p.nsplit;
+      ks = item - (item / p.nsplit) * p.nsplit;
+    }
   } else {
+    const int wg = blockIdx.x;
     const int per = p.total >> 3, rem = p.total & 7, x = wg & 7;
     L = x * per + (x < rem ? x : rem) + (wg >> 3);
   }
@@ -192,9 +250,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
   const int b = bh / p.heads, head = bh - b * p.heads;
   const int i0 = tq * kBM;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 31, hh = lane >> 5;
   // keys [k0, k0 + Nk) of the batch are this workgroup's (all of them unless split)
   int k0 = 0, Nk = p.Nk, kvl = p.lens[b];
   if (split) {
@@ -679,7 +734,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
                           acc[qb][db][4 * g4 + 3]);
     }
     wait_vm<0>();
-    return;
+    continue;
   }
 
   // ---- epilogue: O = O^T / l, bf16.  A lane holds d = 32 db + 8 g4 + 4 hh + 0..3
@@ -716,6 +771,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p) {
     if (irow0 + 4 * it < p.N) *(u32x4*)dst = w;
     dst += 4 * row_stride;
   }
+  if constexpr (!PERSIST) break;
+  }
+}
+
+// the work queue counters of a persistent launch, zeroed before it (a kernel
+// rather than a memset, so that the sequence can be captured in a graph)
+__global__ void zero_queue_kernel(unsigned* queue) {
+  if (threadIdx.x < kQueueCounters)
+    __hip_atomic_store(queue + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- the key splits of the tail tiles combined.  Split s holds O_s and l_s

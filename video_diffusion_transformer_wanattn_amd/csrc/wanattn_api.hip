@@ -155,7 +155,14 @@ wanattn_status check_lens(int32_t B, const int32_t* lens, int32_t maxlen, const 
   return WANATTN_OK;
 }
 
-// Tail splitting of bidirectional self attention.  A launch of T workgroups on
+// Persistent launches and tail splitting of bidirectional self attention.
+// The XCDs of one chip run at measurably different speeds (on some parts the
+// odd ones ~3.5% slower), while a plain launch gives every XCD the same share
+// of workgroups.  With room in the workspace, the self-attention kernel is
+// launched with one workgroup per compute unit, and each workgroup takes query
+// tiles from its XCD's run of tiles, then from the other XCDs' runs, then the
+// split items below (next_item): a fast XCD ends up doing more tiles.
+// A launch of T workgroups on
 // a chip of C compute units runs floor(T / C) full waves of workgroups and then
 // T % C alone, which leaves most of the chip idle for a whole workgroup's time;
 // and the workgroups of the last full wave end over a spread of times (they
@@ -172,6 +179,8 @@ constexpr int kMaxSplit = 8;
 constexpr int kMaxSplitItems = 512;
 constexpr size_t kSplitItemBytes = (size_t)kPartO * sizeof(float4) + (size_t)kBM * sizeof(float2);
 
+constexpr size_t kQueueBytes = 256;  // the persistent launch's queue counters
+
 // split workgroups a self-attention call can use (its workspace holds that many)
 size_t split_items(int32_t B, int32_t N, int32_t heads) {
   const long long nb = B < WANATTN_MAX_LEN_BATCH ? B : WANATTN_MAX_LEN_BATCH;
@@ -179,13 +188,19 @@ size_t split_items(int32_t B, int32_t N, int32_t heads) {
   return (size_t)(wgs < kMaxSplitItems ? wgs : kMaxSplitItems);
 }
 
-// the split (0: none) for a launch of `total` workgroups whose shortest
-// visible key range is minlen, with room for `room` split workgroups
-int choose_split(int total, int minlen, size_t room, int* tail_out) {
+// compute units of the current device (0 if unknown)
+int device_cus() {
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 2)
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
+  return ncu;
+}
+
+// the split (0: none) for a launch of `total` tiles on ncu compute units whose
+// shortest visible key range is minlen, with room for `room` split items
+int choose_split(int total, int ncu, int minlen, size_t room, int* tail_out) {
+  if (ncu < 2) return 0;
   const int rem = total % ncu;
   int tail, nsplit;
   if (rem == 0 && total >= 4 * ncu) {
@@ -201,14 +216,15 @@ int choose_split(int total, int minlen, size_t room, int* tail_out) {
   const int nkt = (minlen + kBN - 1) / kBN;
   while (nsplit > 1 && nkt < 8 * nsplit) --nsplit;
   while (nsplit > 1 && (size_t)tail * nsplit > room) --nsplit;
-  if (nsplit < 2 || ((long long)total - tail + (long long)tail * nsplit) * kThreads > 0xFFFFFFFFll) return 0;
+  if (nsplit < 2) return 0;
   *tail_out = tail;
   return nsplit;
 }
 
 // Launch over groups of at most WANATTN_MAX_LEN_BATCH batches so that the
 // per-batch key lengths always fit the kernel argument block.  `part` (room
-// for part_items split workgroups, or null) enables tail splitting.
+// for part_items split items followed by kQueueBytes, or null) enables
+// persistent launches and tail splitting.
 template <bool ROPE, bool CAUSAL>
 wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStream_t stream,
                            void* part = nullptr, size_t part_items = 0) {
@@ -225,20 +241,26 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
     for (int b = 0; b < nb; ++b) p.lens[b] = lens ? lens[b0 + b] : p.Nk;
     p.total = nb * p.heads * p.ntq;
     if constexpr (ROPE && !CAUSAL) {
-      int minlen = p.Nk, tail = 0;
-      for (int b = 0; b < nb; ++b) minlen = p.lens[b] < minlen ? p.lens[b] : minlen;
-      const int nsplit = part ? choose_split(p.total, minlen, part_items, &tail) : 0;
-      if (nsplit) {
+      const int ncu = part ? device_cus() : 0;
+      if (ncu > 0 && p.total >= ncu) {
+        int minlen = p.Nk, tail = 0;
+        for (int b = 0; b < nb; ++b) minlen = p.lens[b] < minlen ? p.lens[b] : minlen;
+        const int nsplit = choose_split(p.total, ncu, minlen, part_items, &tail);
         p.total -= tail;
-        p.nsplit = nsplit;
+        p.nsplit = nsplit > 0 ? nsplit : 1;
+        p.nsplit_items = tail * nsplit;
         p.part_o = (float4*)part;
         p.part_lb = (float2*)((char*)part + part_items * kPartO * sizeof(float4));
-        hipLaunchKernelGGL((attn_fwd_kernel<ROPE, false, true>), dim3(p.total + tail * nsplit), dim3(kThreads), 0,
-                           stream, p);
+        p.queue = (unsigned*)((char*)part + part_items * kSplitItemBytes);
+        hipLaunchKernelGGL(zero_queue_kernel, dim3(1), dim3(64), 0, stream, p.queue);
+        WA_TRY(launched("queue reset"));
+        hipLaunchKernelGGL((attn_fwd_kernel<ROPE, false, true>), dim3(ncu), dim3(kThreads), 0, stream, p);
         WA_TRY(launched("attention"));
-        MergeParams m{p.part_o, p.part_lb, p.o, p.total, p.ntq, p.heads, p.N, nsplit};
-        hipLaunchKernelGGL(split_merge_kernel, dim3(tail * 8), dim3(256), 0, stream, m);
-        WA_TRY(launched("split merge"));
+        if (nsplit) {
+          MergeParams m{p.part_o, p.part_lb, p.o, p.total, p.ntq, p.heads, p.N, nsplit};
+          hipLaunchKernelGGL(split_merge_kernel, dim3(tail * 8), dim3(256), 0, stream, m);
+          WA_TRY(launched("split merge"));
+        }
         continue;
       }
     }
@@ -580,7 +602,7 @@ wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int3
 
 size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim) {
   if (B < 1 || N < 1 || heads < 1 || head_dim != kHeadDim) return 0;
-  return (size_t)B * N * heads * kHeadDim * 2 + split_items(B, N, heads) * kSplitItemBytes;
+  return (size_t)B * N * heads * kHeadDim * 2 + split_items(B, N, heads) * kSplitItemBytes + kQueueBytes;
 }
 
 wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o, int32_t B,
@@ -591,7 +613,7 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
   t_err[0] = 0;
   WA_TRY(check_theta(theta));
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
-  const size_t items = split_items(B, N, heads), full = bytes + items * kSplitItemBytes;
+  const size_t items = split_items(B, N, heads), full = bytes + items * kSplitItemBytes + kQueueBytes;
   const bool room = workspace_bytes >= full;
   WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
                     workspace_bytes, bytes, room ? full : bytes));
@@ -603,7 +625,8 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
 
 size_t wanattn_self_jitter_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim) {
   if (B < 1 || N < 1 || heads < 1 || heads > kMaxJitterHeads || head_dim != kHeadDim) return 0;
-  return jitter_table_bytes(heads) + (size_t)B * N * heads * kHeadDim * 2 + split_items(B, N, heads) * kSplitItemBytes;
+  return jitter_table_bytes(heads) + (size_t)B * N * heads * kHeadDim * 2 + split_items(B, N, heads) * kSplitItemBytes +
+         kQueueBytes;
 }
 
 wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, void* o, int32_t B,
@@ -616,7 +639,7 @@ wanattn_status wanattn_self_jitter(const void* q, const void* k, const void* v, 
   WA_TRY(check_head_thetas(theta_per_head, heads));
   const size_t tbytes = jitter_table_bytes(heads);
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
-  const size_t items = split_items(B, N, heads), full = tbytes + bytes + items * kSplitItemBytes;
+  const size_t items = split_items(B, N, heads), full = tbytes + bytes + items * kSplitItemBytes + kQueueBytes;
   const bool room = workspace_bytes >= full;
   WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
                     workspace_bytes, tbytes + bytes, room ? full : tbytes + bytes));

@@ -130,7 +130,7 @@ def test_workspace_without_room_turns_the_split_off():
     assert np.array_equal(got_small[:, :, other], got_full[:, :, other])
 
 
-@pytest.mark.parametrize("name", ["wan14b_720p_81f", "wan14b_480p_81f"])
+@pytest.mark.parametrize("name", ["wan14b_720p_81f", "wan14b_480p_81f", "wan14b_480p_165f_causal"])
 def test_every_tile_written_at_full_size(name):
     # the persistent launch hands out every query tile exactly once through
     # its work queues: an output filled with NaN beforehand has none left
@@ -138,6 +138,7 @@ def test_every_tile_written_at_full_size(name):
     t = seeded.workload_tensors(wl, seed=0, cross=False)
     q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
     o = torch.full_like(q, float("nan"))
-    wa.self_attention(q, k, v, (wl.F, wl.H, wl.W), theta=THETA, out=o)
+    wa.self_attention(q, k, v, (wl.F, wl.H, wl.W), theta=THETA, block_causal=wl.block_causal,
+                      chunk_frames=wl.chunk_frames, out=o)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())

@@ -179,7 +179,6 @@ __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t
 
 template <bool ROPE, bool CAUSAL, bool PERSIST = false>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg) {
-  static_assert(!(PERSIST && CAUSAL), "persistent launches are built for the bidirectional mask");
   // LDS: the K' halves of the 4 stages in the first 64 KiB, their V halves in
   // the second, so that every operand read is one base register (per lane)
   // plus an immediate offset below 64 KiB (the ds_read offset field)

@@ -240,12 +240,13 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
     p.o = o0 + (size_t)b0 * qstride;
     for (int b = 0; b < nb; ++b) p.lens[b] = lens ? lens[b0 + b] : p.Nk;
     p.total = nb * p.heads * p.ntq;
-    if constexpr (ROPE && !CAUSAL) {
+    if constexpr (ROPE) {
       const int ncu = part ? device_cus() : 0;
       if (ncu > 0 && p.total >= ncu) {
+        // key splits only under the bidirectional mask
         int minlen = p.Nk, tail = 0;
         for (int b = 0; b < nb; ++b) minlen = p.lens[b] < minlen ? p.lens[b] : minlen;
-        const int nsplit = choose_split(p.total, ncu, minlen, part_items, &tail);
+        const int nsplit = CAUSAL ? 0 : choose_split(p.total, ncu, minlen, part_items, &tail);
         p.total -= tail;
         p.nsplit = nsplit > 0 ? nsplit : 1;
         p.nsplit_items = tail * nsplit;
@@ -254,7 +255,7 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
         p.queue = (unsigned*)((char*)part + part_items * kSplitItemBytes);
         hipLaunchKernelGGL(zero_queue_kernel, dim3(1), dim3(64), 0, stream, p.queue);
         WA_TRY(launched("queue reset"));
-        hipLaunchKernelGGL((attn_fwd_kernel<ROPE, false, true>), dim3(ncu), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<ROPE, CAUSAL, true>), dim3(ncu), dim3(kThreads), 0, stream, p);
         WA_TRY(launched("attention"));
         if (nsplit) {
           MergeParams m{p.part_o, p.part_lb, p.o, p.total, p.ntq, p.heads, p.N, nsplit};
@@ -373,7 +374,7 @@ wanattn_status self_launch(const void* q, const void* k, const void* v, void* o,
   if (mask == WANATTN_MASK_BLOCK_CAUSAL) {
     long long ct = (long long)chunk_frames * grid->H * grid->W;
     p.chunk_tokens = (int)(ct < N ? ct : N);
-    return launch_attn<true, true>(p, B, kv_lens, stream);
+    return launch_attn<true, true>(p, B, kv_lens, stream, part, part_items);
   }
   return launch_attn<true, false>(p, B, kv_lens, stream, part, part_items);
 }

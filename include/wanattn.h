@@ -104,12 +104,15 @@ wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int3
  *   k, v or o, of at least B*N*heads*head_dim*2 bytes: it receives the
  *   rotated keys k' (one rotation per key, shared by every query tile).
  *   wanattn_self_workspace_bytes(B, N, heads, head_dim) adds room for fp32
- *   partial results (at most 512 * 130 KiB): with it, when the bidirectional
- *   launch's last wave of workgroups would fill at most half the chip, those
- *   query tiles run as several workgroups each over ranges of the keys, whose
- *   partial softmax results a second kernel combines.  A smaller workspace
- *   runs without that split.  The contents after the call are unspecified.
- *   Calls that may run concurrently need separate workspaces.
+ *   partial results (at most 512 * 130 KiB) and 256 bytes of work-queue
+ *   counters.  With it, a launch that covers the chip at least once runs one
+ *   workgroup per compute unit, drawing query tiles from one queue per XCD
+ *   (its own first, then the others'), and under the bidirectional mask the
+ *   last query tiles run as several work items each over ranges of the keys,
+ *   whose partial softmax results a second kernel combines.  A smaller
+ *   workspace runs one workgroup per query tile, without the split.  The
+ *   contents after the call are unspecified.  Calls that may run
+ *   concurrently need separate workspaces.
  * Accumulation is fp32; the MFMA operands (rotated and scaled q, rotated k,
  * softmax probabilities, v) are bf16; o is rounded to bf16 (nearest even).
  * Rows of split tiles are combined in a different order, so they can differ

@@ -591,7 +591,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
   //      for keys 16..31 and the block sums of P(j)
   //   (rare, wave-uniform: move the reference, see move_reference)
   //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
-  //      S(j+1) to VGPRs, its mask (tiles that need one) and P(j+1) for keys 0..15
+  //      S(j+1) to VGPRs, its mask (tiles that need one) and P(j+1) for keys 0..15:
+  //      each group is product (row block 0), a pair's exps, product (row block
+  //      1), a K' read, the pair's sum and packing.  One wave issues in order
+  //      and an MFMA leaves the VALU about 4 simple slots: with the two
+  //      products back to back, the first one's slots went unused.
   // so that both phases carry about the same exp work beside their MFMAs
   // The step is written as small groups fenced by scheduling barriers, each an
   // MFMA pair plus the VALU and LDS work meant to run beside it: an MFMA leaves
@@ -660,23 +664,26 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int db = g >> 1, sl = g & 1;
+      const int qb = g >> 2, e = g & 3;  // the pair (keys 2e, 2e+1 of row block qb) of this group
       // O^T += V^T P^T with the accumulator in AGPRs (see acc_fence)
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[0][db]) : "a"(vop[db][sl]), "v"(pb[0][sl]));
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[1][db]) : "a"(vop[db][sl]), "v"(pb[1][sl]));
-      load_kop(SN, kb, g);
       if (g == 0) {
         take_scores();
         if constexpr (decltype(MASKED)::value) mask_scores(j + 1);
-      } else {
-        // pairs (qb, e) = (0, 0..3), (1, 0..3) over groups 1..7, two in group 1
-        const int pr = g == 1 ? 0 : g;
-        exp_pair(pr >> 2, 0, pr & 3, pk0[pr >> 2], h0[pr >> 2]);
-        asm volatile("" : "+v"(pk0[pr >> 2][pr & 3]), "+v"(h0[pr >> 2][pr & 1]));
-        if (g == 1) {
-          exp_pair(0, 0, 1, pk0[0], h0[0]);
-          asm volatile("" : "+v"(pk0[0][1]), "+v"(h0[0][1]));
-        }
       }
+      // the exps after this product, not hoisted above it (the two products
+      // of a group would otherwise issue back to back)
+      asm volatile("" : "+v"(sv[qb][2 * e]), "+v"(sv[qb][2 * e + 1]));
+      float p0 = __builtin_amdgcn_exp2f(sv[qb][2 * e]);
+      float p1 = __builtin_amdgcn_exp2f(sv[qb][2 * e + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[1][db]) : "a"(vop[db][sl]), "v"(pb[1][sl]));
+      asm volatile("" : "+v"(p0), "+v"(p1));
+      load_kop(SN, kb, g);
+      if (e < 2) h0[qb][e & 1] = p0 + p1;
+      else h0[qb][e & 1] += p0 + p1;
+      pk0[qb][e] = pack_bf16x2(p0, p1);
+      asm volatile("" : "+v"(pk0[qb][e]), "+v"(h0[qb][e & 1]));
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll

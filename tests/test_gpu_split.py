@@ -142,3 +142,23 @@ def test_every_tile_written_at_full_size(name):
                       chunk_frames=wl.chunk_frames, out=o)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
+
+
+def test_full_size_two_batches_with_kv_lens():
+    # 32,760 tokens x 40 heads, two batches with 32,760 and 20,000 visible keys:
+    # 10,240 tiles = 40 whole waves on 256 CUs, so the last wave (batch 1's
+    # last heads) runs as key ranges taken from the shorter batch's length;
+    # sampled rows of both batches, every head
+    wl = seeded.WORKLOADS["wan14b_480p_81f"]
+    grid = (wl.F, wl.H, wl.W)
+    B, lens = 2, [wl.N, 20000]
+    q, k = (gen((B, wl.N, wl.heads, 128), 915, s, 1.0) for s in (1, 2))
+    v = gen((B, wl.N, wl.heads, 128), 915, 3, 0.5)
+    o = wa.self_attention(to_dev(q), to_dev(k), to_dev(v), grid, theta=THETA, kv_lens=lens)
+    torch.cuda.synchronize()
+    rows = seeded.sample_rows(wl.N, 24, seed=915, must=(wl.N - 1, wl.N - 257, 19999, 20000))
+    got = from_dev(o[:, torch.from_numpy(rows.astype(np.int64)).cuda()])
+    assert bool(torch.isfinite(o.float()).all())
+    del o
+    ref = oracle.self_rows(q, k, v, grid, rows=rows, theta=THETA, kv_lens=lens)
+    assert_parity(got, ref, what="two batches with kv_lens at full size")

@@ -40,7 +40,8 @@
 // loaded, so p = exp2(s - m) maps to v_exp_f32, and the subtraction of the row
 // reference m is folded into the QK^T product: its first k-step starts from an
 // accumulator tile holding -m instead of zero.  The O accumulators live in
-// AGPRs (the PV products are inline asm, see acc_fence).  The reference starts at the max of the first block and is only moved when a
+// AGPRs (the PV products are inline asm, see acc_fence).  The reference
+// starts at the max of the first block and is only moved when a
 // lane's block sum of p exceeds 2^16 (some p above 2^12, or an overflow), which
 // makes the O rescale rare; the result is the same softmax (the final division
 // by the running sum uses the same reference point).
@@ -200,588 +201,589 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
 
   // one work item per pass; a plain launch makes one pass
   for (;;) {
-  // A persistent pass reads the arguments again from the kernel argument
-  // segment (through a pointer the compiler cannot see through) and derives
-  // the lane constants again: otherwise they are all kept in registers across
-  // passes (~100 SGPRs and ~80 VGPRs of spills).
-  const auto& p = [&]() -> decltype(auto) {
+    // A persistent pass reads the arguments again from the kernel argument
+    // segment (through a pointer the compiler cannot see through) and derives
+    // the lane constants again: otherwise they are all kept in registers across
+    // passes (~100 SGPRs and ~80 VGPRs of spills).
+    const auto& p = [&]() -> decltype(auto) {
+      if constexpr (PERSIST) {
+        auto kp = (const __attribute__((address_space(4))) AttnParams*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(kp));
+        return *kp;
+      } else {
+        return (const AttnParams&)p_arg;
+      }
+    }();
+    int tid = threadIdx.x;
+    if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, hh = lane >> 5;
+    // ---- work item -> (batch, head, query tile).  A plain launch runs workgroup w
+    // on XCD w % 8; it gives each XCD a contiguous run of tiles so that the
+    // concurrent workgroups of an XCD walk the same head's K/V through their
+    // shared L2.  A persistent launch keeps those runs as the XCDs' queues.
+    // A split item takes key range ks of tile total + item / nsplit.
+    int L, ks = 0, item = 0;
+    bool split = false;
     if constexpr (PERSIST) {
-      auto kp = (const __attribute__((address_space(4))) AttnParams*)__builtin_amdgcn_kernarg_segment_ptr();
-      asm volatile("" : "+s"(kp));
-      return *kp;
+      // every thread has read the previous item (its pass had barriers since)
+      if (tid == 0) s_item = next_item(p_arg, xcc, cursor);
+      __syncthreads();
+      const int it = s_item;
+      if (it < 0) break;
+      split = it >= p.total;
+      L = it;
+      if (split) {
+        item = it - p.total;
+        L = p.total + item / p.nsplit;
+        ks = item - (item / p.nsplit) * p.nsplit;
+      }
     } else {
-      return (const AttnParams&)p_arg;
+      const int wg = blockIdx.x;
+      const int per = p.total >> 3, rem = p.total & 7, x = wg & 7;
+      L = x * per + (x < rem ? x : rem) + (wg >> 3);
     }
-  }();
-  int tid = threadIdx.x;
-  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 31, hh = lane >> 5;
-  // ---- work item -> (batch, head, query tile).  A plain launch runs workgroup w
-  // on XCD w % 8; it gives each XCD a contiguous run of tiles so that the
-  // concurrent workgroups of an XCD walk the same head's K/V through their
-  // shared L2.  A persistent launch keeps those runs as the XCDs' queues.
-  // A split item takes key range ks of tile total + item / nsplit.
-  int L, ks = 0, item = 0;
-  bool split = false;
-  if constexpr (PERSIST) {
-    // every thread has read the previous item (its pass had barriers since)
-    if (tid == 0) s_item = next_item(p_arg, xcc, cursor);
-    __syncthreads();
-    const int it = s_item;
-    if (it < 0) break;
-    split = it >= p.total;
-    L = it;
+    const int bh = L / p.ntq;
+    int tq = L - bh * p.ntq;
+    if (CAUSAL) tq = p.ntq - 1 - tq;  // heaviest tiles of a head first
+    const int b = bh / p.heads, head = bh - b * p.heads;
+    const int i0 = tq * kBM;
+
+    // keys [k0, k0 + Nk) of the batch are this workgroup's (all of them unless split)
+    int k0 = 0, Nk = p.Nk, kvl = p.lens[b];
     if (split) {
-      item = it - p.total;
-      L = p.total + item / p.nsplit;
-      ks = item - (item / p.nsplit) * p.nsplit;
+      // the host launches splits only where every range holds a key
+      const int nkt = (kvl + kBN - 1) / kBN;
+      const int t_lo = ks * nkt / p.nsplit, t_hi = (ks + 1) * nkt / p.nsplit;
+      k0 = t_lo * kBN;
+      Nk = min(t_hi * kBN, kvl) - k0;
+      kvl = Nk;
     }
-  } else {
-    const int wg = blockIdx.x;
-    const int per = p.total >> 3, rem = p.total & 7, x = wg & 7;
-    L = x * per + (x < rem ? x : rem) + (wg >> 3);
-  }
-  const int bh = L / p.ntq;
-  int tq = L - bh * p.ntq;
-  if (CAUSAL) tq = p.ntq - 1 - tq;  // heaviest tiles of a head first
-  const int b = bh / p.heads, head = bh - b * p.heads;
-  const int i0 = tq * kBM;
+    const int i_last = min(i0 + kBM, p.N) - 1;
+    const int kv_end = row_limit<CAUSAL>(p, kvl, i_last);
+    const int kv_full = row_limit<CAUSAL>(p, kvl, i0);
+    const int nt = (kv_end + kBN - 1) / kBN;
+    const int nb = 2 * nt;
 
-  // keys [k0, k0 + Nk) of the batch are this workgroup's (all of them unless split)
-  int k0 = 0, Nk = p.Nk, kvl = p.lens[b];
-  if (split) {
-    // the host launches splits only where every range holds a key
-    const int nkt = (kvl + kBN - 1) / kBN;
-    const int t_lo = ks * nkt / p.nsplit, t_hi = (ks + 1) * nkt / p.nsplit;
-    k0 = t_lo * kBN;
-    Nk = min(t_hi * kBN, kvl) - k0;
-    kvl = Nk;
-  }
-  const int i_last = min(i0 + kBM, p.N) - 1;
-  const int kv_end = row_limit<CAUSAL>(p, kvl, i_last);
-  const int kv_full = row_limit<CAUSAL>(p, kvl, i0);
-  const int nt = (kv_end + kBN - 1) / kBN;
-  const int nb = 2 * nt;
+    const size_t row_stride = (size_t)p.heads * kHeadDim;  // elements between tokens
+    const uint32_t rsb = (uint32_t)(row_stride * 2);        // bytes between tokens
+    const uint16_t* qbase = p.q + ((size_t)b * p.N * p.heads + head) * kHeadDim;
+    const char* kbase = (const char*)(p.k + (((size_t)b * p.Nk + k0) * p.heads + head) * kHeadDim);
+    const char* vbase = (const char*)(p.v + (((size_t)b * p.Nk + k0) * p.heads + head) * kHeadDim);
 
-  const size_t row_stride = (size_t)p.heads * kHeadDim;  // elements between tokens
-  const uint32_t rsb = (uint32_t)(row_stride * 2);        // bytes between tokens
-  const uint16_t* qbase = p.q + ((size_t)b * p.N * p.heads + head) * kHeadDim;
-  const char* kbase = (const char*)(p.k + (((size_t)b * p.Nk + k0) * p.heads + head) * kHeadDim);
-  const char* vbase = (const char*)(p.v + (((size_t)b * p.Nk + k0) * p.heads + head) * kHeadDim);
-
-  // ---- tile loads straight into LDS.  Instruction i of wave w fills 1 KiB:
-  // rows m = 16w + 4i + l/16 (l = lane), stored chunk l%16 holding global chunk
-  // (l%16) ^ swizzle(m).  K row m holds key k_slot(m) = 16w + 4 swap01(i) + l/16.
-  // Full tiles: a uniform row base plus a fixed per-lane offset.  The last,
-  // partial tile clamps every row to the last key (those rows are masked).
-  const int ld_row = lane >> 4, ld_chunk = lane & 15;
-  // byte offsets from the tile's first key, the row of each load included, so
-  // that all loads of a tile share one scalar base (64 rows fit in 32 bits:
-  // the library limits heads so that 64 token rows span less than 2^31 bytes)
-  uint32_t koff_ld[4], voff_ld[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int krow = 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
-    const int vrow = 16 * wave + 4 * i;
-    koff_ld[i] = (krow + ld_row) * rsb + 16 * (ld_chunk ^ (4 * i + ld_row));
-    voff_ld[i] = (vrow + ld_row) * rsb + 16 * (ld_chunk ^ (4 * ld_row));
-  }
-  // a tile known to hold kBN keys
-  auto issue_full_tile = [&](auto S, int t) __attribute__((always_inline)) {
-    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
-    const char* kt = kbase + (size_t)t * kBN * rsb;
-    const char* vt = vbase + (size_t)t * kBN * rsb;
-#pragma unroll
+    // ---- tile loads straight into LDS.  Instruction i of wave w fills 1 KiB:
+    // rows m = 16w + 4i + l/16 (l = lane), stored chunk l%16 holding global chunk
+    // (l%16) ^ swizzle(m).  K row m holds key k_slot(m) = 16w + 4 swap01(i) + l/16.
+    // Full tiles: a uniform row base plus a fixed per-lane offset.  The last,
+    // partial tile clamps every row to the last key (those rows are masked).
+    const int ld_row = lane >> 4, ld_chunk = lane & 15;
+    // byte offsets from the tile's first key, the row of each load included, so
+    // that all loads of a tile share one scalar base (64 rows fit in 32 bits:
+    // the library limits heads so that 64 token rows span less than 2^31 bytes)
+    uint32_t koff_ld[4], voff_ld[4];
+  #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int blk = 4 * wave + i;
-      dma16(kt, koff_ld[i], st + blk * 1024);
-      dma16(vt, voff_ld[i], st + kVHalves + blk * 1024);
+      const int krow = 16 * wave + 4 * ((i >> 1) | ((i & 1) << 1));
+      const int vrow = 16 * wave + 4 * i;
+      koff_ld[i] = (krow + ld_row) * rsb + 16 * (ld_chunk ^ (4 * i + ld_row));
+      voff_ld[i] = (vrow + ld_row) * rsb + 16 * (ld_chunk ^ (4 * ld_row));
     }
-  };
-  // load n (0..7) of a full tile: K (n even) or V (n odd) rows of group n / 2
-  auto issue_one = [&](auto S, int t, int n) __attribute__((always_inline)) {
-    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
-    const int i = n >> 1, blk = 4 * wave + i;
-    if (n & 1) dma16(vbase + (size_t)t * kBN * rsb, voff_ld[i], st + kVHalves + blk * 1024);
-    else dma16(kbase + (size_t)t * kBN * rsb, koff_ld[i], st + blk * 1024);
-  };
-  auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {
-    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
-    const char* kt = kbase + (size_t)t * kBN * rsb;
-    const char* vt = vbase + (size_t)t * kBN * rsb;
-    if (t * kBN + kBN <= Nk) {
-      issue_full_tile(S, t);
-    } else {
-#pragma unroll
+    // a tile known to hold kBN keys
+    auto issue_full_tile = [&](auto S, int t) __attribute__((always_inline)) {
+      const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
+      const char* kt = kbase + (size_t)t * kBN * rsb;
+      const char* vt = vbase + (size_t)t * kBN * rsb;
+  #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int blk = 4 * wave + i;
-        const int m = 4 * blk + ld_row;
-        const int kkey = min(t * kBN + k_slot(m), Nk - 1) - t * kBN;
-        const int vkey = min(t * kBN + m, Nk - 1) - t * kBN;
-        dma16(kt, (uint32_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m)), st + blk * 1024);
-        dma16(vt, (uint32_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m)), st + kVHalves + blk * 1024);
+        dma16(kt, koff_ld[i], st + blk * 1024);
+        dma16(vt, voff_ld[i], st + kVHalves + blk * 1024);
       }
-    }
-  };
-
-  // the look-ahead scoring of the block after the last one reads the next
-  // stage: with fewer tiles than stages that stage was never filled, so zero
-  // the stages then (with more, it holds an earlier tile: finite values whose
-  // scores are discarded).  nt is uniform over the workgroup.
-  if (nt < kStages) {
-#pragma unroll
-    for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i) *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
-    tile_barrier();
-  }
-
-  // prefetch the first two tiles while the queries are loaded
-  issue_tile(S0{}, 0);
-  if (nt > 1) issue_tile(S1{}, 1);
-
-  // ---- Q: load, rotate, scale, round to bf16; kept in registers as the B
-  // operand of K Q^T: lane holds d = 16 kk + 8 hh + 0..7 of its query.
-  // All 16 loads are issued before any is used (a pin per chunk made the
-  // compiler wait for each load in turn: ~7 us per workgroup).
-  bf16x8 qf[2][8];
-  int lim[2];
-  const float2* qtab = p.tab + (size_t)head * p.tab_hstride;
-  u32x4 qraw[2][8];
-  int pf[2] = {0, 0}, ph[2] = {0, 0}, pw[2] = {0, 0};
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int i = i0 + wave * 64 + qb * 32 + r;
-    const int ic = i < p.N ? i : p.N - 1;
-    lim[qb] = row_limit<CAUSAL>(p, kvl, ic);
-    if (ROPE) {
-      int f, rm, h, w;
-      divmod(ic, p.H * p.W, p.inv_hw, f, rm);
-      divmod(rm, p.W, p.inv_w, h, w);
-      pf[qb] = f + p.f0;
-      ph[qb] = h + p.h0;
-      pw[qb] = w + p.w0;
-    }
-    const u32x4* src = (const u32x4*)(qbase + (size_t)ic * row_stride);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qraw[qb][kk] = src[2 * kk + hh];
-  }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      u32x4 pk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pk[e] = rotate_pair<ROPE>(qraw[qb][kk][e], qtab, 8 * kk + 4 * hh + e, pf[qb], ph[qb], pw[qb], p.qscale);
-      qf[qb][kk] = __builtin_bit_cast(bf16x8, pk);
-    }
-  // keep Q in AGPRs: the MFMA reads its B operand from there directly and the
-  // arch VGPRs stay free for the scores and the softmax
-  asm volatile(""
-               : "+a"(qf[0][0]), "+a"(qf[0][1]), "+a"(qf[0][2]), "+a"(qf[0][3]), "+a"(qf[0][4]), "+a"(qf[0][5]),
-                 "+a"(qf[0][6]), "+a"(qf[0][7]), "+a"(qf[1][0]), "+a"(qf[1][1]), "+a"(qf[1][2]), "+a"(qf[1][3]),
-                 "+a"(qf[1][4]), "+a"(qf[1][5]), "+a"(qf[1][6]), "+a"(qf[1][7]));
-
-  floatx16 acc[2][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[qb][db][j] = 0.0f;
-  // The O products (phase B below) are inline asm so that their accumulators
-  // live in AGPRs for the whole loop: the arch VGPRs then hold the scores,
-  // the operands and the loop invariants without parking any of them in AGPRs
-  // (which cost ~20 copies per block).  The compiler does not know these asm
-  // statements are MFMAs and inserts no wait states around them, so this fence
-  // does: 24 wait states (more than the 8-pass MFMA's result latency) before
-  // any VALU access of O after an O product, and after VALU writes of O
-  // (initialisation, rescale) before the next product reads them.  Dependent
-  // MFMA -> MFMA accumulation needs none (the hardware interlocks it).
-  auto acc_fence = [&]() __attribute__((always_inline)) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
-                   "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
-  };
-  acc_fence();
-  // Running softmax reference per query row, kept as a bias b = -m added to the
-  // scores inside the QK^T product: the first k-step of the product starts
-  // from an accumulator tile holding b (every value a lane holds in S^T
-  // belongs to its own query column, so the tile is b repeated).  The scores
-  // come out of the product already shifted, and p = exp2(s) needs no
-  // subtraction; the tile only changes when the reference moves.
-  float bias[2] = {0.0f, 0.0f}, lrun[2] = {0.0f, 0.0f};
-  floatx16 btile[2];
-  auto set_bias = [&](int qb, float b) __attribute__((always_inline)) {
-    bias[qb] = b;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) btile[qb][e] = b;
-  };
-  set_bias(0, 0.0f);
-  set_bias(1, 0.0f);
-
-  // LDS operand offsets inside a stage.  K: row r (+32 kb), stored chunk
-  // (2 kk + hh) ^ (r & 15).  V (transposed reads): lane (vg, vu, vq) supplies
-  // key 8 (vg>>1) + vu (+ 32 kb + 16 sl + 4 e) and d 32 db + 16 (vg&1) + 4 vq,
-  // whose chunk 4 db + 2 (vg&1) + vq/2 is stored at 4 (db ^ vu) + 2 (vg&1) + vq/2.
-  int koff[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    koff[kk] = r * kRowBytes + 16 * ((2 * kk + hh) ^ (r & 15));
-    asm volatile("" : "+v"(koff[kk]));
-  }
-  const int vg = lane >> 4, vu = (lane & 15) >> 2, vq = lane & 3;
-  int voff[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    voff[db] = kVHalves + (8 * (vg >> 1) + vu) * kRowBytes +
-               16 * (4 * (db ^ vu) + 2 * (vg & 1) + (vq >> 1)) + 8 * (vq & 1);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(voff[db]));
-
-  bf16x8 kop[8];      // K' operands of the next block to score
-  bf16x8 vop[4][2];   // V operands of the block being accumulated
-  float sv[2][16];    // scores of the block being finished (base 2, VGPR copy)
-  floatx16 sacc[2];   // MFMA accumulators of the block being scored
-  bf16x8 pcar[2];     // P of keys 0..15 of the block being finished, taken one phase early
-  float scar[2];      // and this lane's sums of them
-
-  auto load_kops = [&](auto S, int kb) __attribute__((always_inline)) {
-    const char* kt = stage(S) + kb * 32 * kRowBytes;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kop[kk] = *(const bf16x8*)(kt + koff[kk]);
-  };
-  // single operand reads, for the hand-ordered block step
-  auto load_kop = [&](auto S, int kb, int kk) __attribute__((always_inline)) {
-    kop[kk] = *(const bf16x8*)(stage(S) + kb * 32 * kRowBytes + koff[kk]);
-  };
-  auto load_vop = [&](auto S, int kb, int db, int sl) __attribute__((always_inline)) {
-    const char* vt = stage(S) + kb * 32 * kRowBytes;
-    shortx4 tr[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      tr[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) shortx4*)(vt + (16 * sl + 4 * e) * kRowBytes + voff[db]));
-    // whole-vector casts: assembling this operand element by element was
-    // lowered to a splat of element 0 by the compiler
-    vop[db][sl] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, tr[0]), __builtin_bit_cast(bf16x4, tr[1]),
-                                          0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  auto qk = [&]() __attribute__((always_inline)) {
-    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[0][0], btile[0], 0, 0, 0);
-    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[1][0], btile[1], 0, 0, 0);
-#pragma unroll
-    for (int kk = 1; kk < 8; ++kk) {
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
-    }
-  };
-  // exp2 of the shifted scores in sv: bf16 operands of the PV product and this
-  // lane's fp32 block sums.  One pair of probabilities (keys 16 sl + 2 e, + 1)
-  // of row block qb: packed word into pk[e], sum into acc2[e & 1].  (Plain adds:
-  // the dot-product VALU instructions wait for the MFMA pipe to drain.)
-  auto exp_pair = [&](int qb, int sl, int e, u32x4& pk, float (&acc2)[2]) __attribute__((always_inline)) {
-    const float p0 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e]);
-    const float p1 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1]);
-    // pairs e = 0, 1 start the two partial sums (every caller takes e in
-    // order 0..3): assigning rather than adding to 0 saves an add, which the
-    // compiler may not drop itself (0 + x is not x for x = -0)
-    if (e < 2) acc2[e & 1] = p0 + p1;
-    else acc2[e & 1] += p0 + p1;
-    pk[e] = pack_bf16x2(p0, p1);
-  };
-  // (half sl of the block: keys 16 sl .. 16 sl + 15, registers 8 sl .. 8 sl + 7)
-  auto exp_half = [&](int qb, int sl, bf16x8& out, float& sum) __attribute__((always_inline)) {
-    float acc2[2] = {0.0f, 0.0f};
-    u32x4 pk;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) exp_pair(qb, sl, e, pk, acc2);
-    out = __builtin_bit_cast(bf16x8, pk);
-    sum = acc2[0] + acc2[1];
-  };
-  auto softmax_exp_row = [&](int qb, bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
-    float h0, h1;
-    exp_half(qb, 0, pb[qb][0], h0);
-    exp_half(qb, 1, pb[qb][1], h1);
-    bsum[qb] = h0 + h1;
-  };
-  // copy the scored block to VGPRs
-  auto take_scores = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sv[qb][e] = sacc[qb][e];
-  };
-  // visibility of block j: key of register e is 32 j + 16 (e/8) + 8 hh + e%8
-  auto mask_scores = [&](int j) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = 32 * j + 16 * (e >> 3) + 8 * hh + (e & 7);
-        if (key >= lim[qb]) sv[qb][e] = -__builtin_inff();
+    };
+    // load n (0..7) of a full tile: K (n even) or V (n odd) rows of group n / 2
+    auto issue_one = [&](auto S, int t, int n) __attribute__((always_inline)) {
+      const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
+      const int i = n >> 1, blk = 4 * wave + i;
+      if (n & 1) dma16(vbase + (size_t)t * kBN * rsb, voff_ld[i], st + kVHalves + blk * 1024);
+      else dma16(kbase + (size_t)t * kBN * rsb, koff_ld[i], st + blk * 1024);
+    };
+    auto issue_tile = [&](auto S, int t) __attribute__((always_inline)) {
+      const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S);
+      const char* kt = kbase + (size_t)t * kBN * rsb;
+      const char* vt = vbase + (size_t)t * kBN * rsb;
+      if (t * kBN + kBN <= Nk) {
+        issue_full_tile(S, t);
+      } else {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int blk = 4 * wave + i;
+          const int m = 4 * blk + ld_row;
+          const int kkey = min(t * kBN + k_slot(m), Nk - 1) - t * kBN;
+          const int vkey = min(t * kBN + m, Nk - 1) - t * kBN;
+          dma16(kt, (uint32_t)kkey * rsb + 16 * (ld_chunk ^ k_swz(m)), st + blk * 1024);
+          dma16(vt, (uint32_t)vkey * rsb + 16 * (ld_chunk ^ v_swz(m)), st + kVHalves + blk * 1024);
+        }
       }
-  };
-  auto row_max = [&](int qb) __attribute__((always_inline)) -> float {
-    float m0 = fmaxf(sv[qb][0], sv[qb][1]);
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(sv[qb][e], sv[qb][e + 1]));
-    return wave_half_max(m0);
-  };
-  // Lazy reference (rare after the first blocks).  The probabilities of block
-  // j were taken against the current reference; when a lane's partial block
-  // sum exceeds kLazySum (some p above 2^12, or an overflow to inf), every row
-  // whose block max lies above its reference moves the reference to that max:
-  // O and l are scaled by 2^(b_new - b_old), block j's probabilities are taken
-  // again, and the scores of block j+1 (already formed against the old
-  // reference) are shifted alike.  One wave-uniform branch for both row blocks.
-  auto move_reference = [&](bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
-    acc_fence();
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m = row_max(qb);
-      const float old = bias[qb];
-      set_bias(qb, m > 0.0f ? old - m : old);
-      const float delta = bias[qb] - old;
-      const float alpha = __builtin_amdgcn_exp2f(delta);
-      lrun[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[qb][db][e] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sv[qb][e] += delta;
-        sacc[qb][e] += delta;
-      }
-      softmax_exp_row(qb, pb, bsum);
-    }
-    acc_fence();
-    // P was just rewritten by VALU and is read next by the O products
-    asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
-  };
+    };
 
-  // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored and
-  // finished, K' operands of block 1 loaded
-  if (nt > 1) wait_vm<8>();
-  else wait_vm<0>();
-  tile_barrier();
-  if (nt > 2) issue_tile(S2{}, 2);
-  load_kops(S0{}, 0);
-  qk();
-  load_kops(S0{}, 1);
-  {
-    // block 0 was scored with b = 0; its row max becomes the first reference
-    // (every row sees key 0, so the max is finite; O and l are still zero)
-    take_scores();
-    if (32 > kv_full) mask_scores(0);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      set_bias(qb, -row_max(qb));
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sv[qb][e] += bias[qb];
-      exp_half(qb, 0, pcar[qb], scar[qb]);
-    }
-  }
-
-  // ---- main pipeline.  Block j of tile t (stage S) with j = 2t + kb:
-  //   (first block of a tile: tile t+1 resident, tile t+3 requested)
-  //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T + b  next to  P(j) = exp2(S(j))
-  //      for keys 16..31 and the block sums of P(j)
-  //   (rare, wave-uniform: move the reference, see move_reference)
-  //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
-  //      S(j+1) to VGPRs, its mask (tiles that need one) and P(j+1) for keys 0..15:
-  //      each group is product (row block 0), a pair's exps, product (row block
-  //      1), a K' read, the pair's sum and packing.  One wave issues in order
-  //      and an MFMA leaves the VALU about 4 simple slots: with the two
-  //      products back to back, the first one's slots went unused.
-  // so that both phases carry about the same exp work beside their MFMAs
-  // The step is written as small groups fenced by scheduling barriers, each an
-  // MFMA pair plus the VALU and LDS work meant to run beside it: an MFMA leaves
-  // the VALU only part of its cycles, so that work must be spread evenly.
-  // MASKED steps (the tail loop) check at run time which tiles exist; the
-  // others (the unrolled main loop) only run where tiles t+1..t+3 exist and
-  // t+3 is full, and need no element mask.
-  auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
-    const int j = 2 * t + kb;
-    if constexpr (!decltype(MASKED)::value) {
-      // the loads of tile t+3 are spread over the QK^T groups below
-      if (kb == 0) {
-        wait_vm<8>();
-        tile_barrier();
-      }
-    } else if (kb == 0 && t + 1 < nt) {
-      if (t + 2 < nt) wait_vm<8>();
-      else wait_vm<0>();
+    // the look-ahead scoring of the block after the last one reads the next
+    // stage: with fewer tiles than stages that stage was never filled, so zero
+    // the stages then (with more, it holds an earlier tile: finite values whose
+    // scores are discarded).  nt is uniform over the workgroup.
+    if (nt < kStages) {
+  #pragma unroll
+      for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i)
+        *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
       tile_barrier();
-      if (t + 3 < nt) issue_tile(SNN, t + 3);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- phase A: S(j+1) = K'(j+1) Q'^T + b; P(j) for keys 16..31; V(j) operands
-    // lgkmcnt(0), as an instruction the compiler accounts for: the K' operands
-    // read during the previous phase are complete here, so no drain is needed
-    // later in this phase, after the V reads below have been issued
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    u32x4 pk1[2];
-    float h1[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    load_vop(S, kb, 0, 0);
-    load_vop(S, kb, 0, 1);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], kk == 0 ? btile[0] : sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], kk == 0 ? btile[1] : sacc[1], 0, 0, 0);
-      exp_pair(kk >> 2, 1, kk & 3, pk1[kk >> 2], h1[kk >> 2]);
-      // keep the packed word here: it is only read after the check below,
-      // and would otherwise be sunk past it
-      asm volatile("" : "+v"(pk1[kk >> 2][kk & 3]));
-      if (kk < 6) load_vop(S, kb, 1 + kk / 2, kk & 1);
-      if constexpr (!decltype(MASKED)::value) {
-        if (kb == 0) issue_one(SNN, t + 3, kk);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    bf16x8 pb[2][2];
-    float bsum[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      pb[qb][0] = pcar[qb];
-      pb[qb][1] = __builtin_bit_cast(bf16x8, pk1[qb]);
-      bsum[qb] = scar[qb] + (h1[qb][0] + h1[qb][1]);
-    }
-    // rare: marked unlikely so that the rescale is placed out of line and the
-    // common path runs on without a taken branch (inline, every block ended in a
-    // jump over it)
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(fmaxf(bsum[0], bsum[1]) > kLazySum) != 0, 0))
-      move_reference(pb, bsum);
-    lrun[0] += bsum[0];
-    lrun[1] += bsum[1];
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- phase B: O += V(j)^T P(j)^T; K'(j+2) operands; S(j+1) to VGPRs (and
-    // its mask); P(j+1) for keys 0..15
-    u32x4 pk0[2];
-    float h0[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int db = g >> 1, sl = g & 1;
-      const int qb = g >> 2, e = g & 3;  // the pair (keys 2e, 2e+1 of row block qb) of this group
-      // O^T += V^T P^T with the accumulator in AGPRs (see acc_fence)
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[0][db]) : "a"(vop[db][sl]), "v"(pb[0][sl]));
-      if (g == 0) {
-        take_scores();
-        if constexpr (decltype(MASKED)::value) mask_scores(j + 1);
-      }
-      // the exps after this product, not hoisted above it (the two products
-      // of a group would otherwise issue back to back)
-      asm volatile("" : "+v"(sv[qb][2 * e]), "+v"(sv[qb][2 * e + 1]));
-      float p0 = __builtin_amdgcn_exp2f(sv[qb][2 * e]);
-      float p1 = __builtin_amdgcn_exp2f(sv[qb][2 * e + 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[1][db]) : "a"(vop[db][sl]), "v"(pb[1][sl]));
-      asm volatile("" : "+v"(p0), "+v"(p1));
-      load_kop(SN, kb, g);
-      if (e < 2) h0[qb][e & 1] = p0 + p1;
-      else h0[qb][e & 1] += p0 + p1;
-      pk0[qb][e] = pack_bf16x2(p0, p1);
-      asm volatile("" : "+v"(pk0[qb][e]), "+v"(h0[qb][e & 1]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      pcar[qb] = __builtin_bit_cast(bf16x8, pk0[qb]);
-      scar[qb] = h0[qb][0] + h0[qb][1];
-    }
-  };
-  using NoMask = std::integral_constant<bool, false>;
-  using Mask = std::integral_constant<bool, true>;
-  // Block j+1 (scored in step j) needs the element mask iff 32 (j+1) + 32 > kv_full,
-  // i.e. from block jm = kv_full / 32 on.  Whole tiles whose steps score only
-  // earlier blocks, and for which tile t+3 exists and is full, run in the
-  // unrolled loop with compile-time stages; the rest (the last few tiles, or
-  // the chunk a causal query tile straddles) run in a loop with run-time stages.
-  const int jm = kv_full / 32;
-  const int tm = max(0, min(min(nt, (jm - 1) / 2), Nk / kBN - 3));
-  auto tile_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t) __attribute__((always_inline)) {
-    block_step(S, SN, SNN, MASKED, t, 0);
-    block_step(S, SN, SNN, MASKED, t, 1);
-  };
-  // unrolled over 8 tiles (the loop-carried scores and operands then return
-  // to their registers without the copies a 4-tile body needed), then 4
-  int t = 0;
-  for (; t + 8 <= tm; t += 8) {
-    tile_step(S0{}, S1{}, S3{}, NoMask{}, t);
-    tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 1);
-    tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 2);
-    tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 3);
-    tile_step(S0{}, S1{}, S3{}, NoMask{}, t + 4);
-    tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 5);
-    tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 6);
-    tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 7);
-  }
-  for (; t + 4 <= tm; t += 4) {
-    tile_step(S0{}, S1{}, S3{}, NoMask{}, t);
-    tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 1);
-    tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 2);
-    tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 3);
-  }
-  for (; t < nt; ++t) tile_step(t, t + 1, t + 3, Mask{}, t);
 
-  if (split) {
-    // ---- partial epilogue: O, l and the bias as they stand, fp32, one
-    // whole 1 KiB run of float4 per store instruction
-    acc_fence();
-    float4* po = p.part_o + (size_t)item * kPartO + (size_t)(2 * wave) * 16 * 64 + lane;
-#pragma unroll
+    // prefetch the first two tiles while the queries are loaded
+    issue_tile(S0{}, 0);
+    if (nt > 1) issue_tile(S1{}, 1);
+
+    // ---- Q: load, rotate, scale, round to bf16; kept in registers as the B
+    // operand of K Q^T: lane holds d = 16 kk + 8 hh + 0..7 of its query.
+    // All 16 loads are issued before any is used (a pin per chunk made the
+    // compiler wait for each load in turn: ~7 us per workgroup).
+    bf16x8 qf[2][8];
+    int lim[2];
+    const float2* qtab = p.tab + (size_t)head * p.tab_hstride;
+    u32x4 qraw[2][8];
+    int pf[2] = {0, 0}, ph[2] = {0, 0}, pw[2] = {0, 0};
+  #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float l = wave_half_sum(lrun[qb]);
-      if (hh == 0) p.part_lb[(size_t)item * kBM + (2 * wave + qb) * 32 + r] = make_float2(l, bias[qb]);
-#pragma unroll
+      const int i = i0 + wave * 64 + qb * 32 + r;
+      const int ic = i < p.N ? i : p.N - 1;
+      lim[qb] = row_limit<CAUSAL>(p, kvl, ic);
+      if (ROPE) {
+        int f, rm, h, w;
+        divmod(ic, p.H * p.W, p.inv_hw, f, rm);
+        divmod(rm, p.W, p.inv_w, h, w);
+        pf[qb] = f + p.f0;
+        ph[qb] = h + p.h0;
+        pw[qb] = w + p.w0;
+      }
+      const u32x4* src = (const u32x4*)(qbase + (size_t)ic * row_stride);
+  #pragma unroll
+      for (int kk = 0; kk < 8; ++kk) qraw[qb][kk] = src[2 * kk + hh];
+    }
+  #pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+  #pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        u32x4 pk;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pk[e] = rotate_pair<ROPE>(qraw[qb][kk][e], qtab, 8 * kk + 4 * hh + e, pf[qb], ph[qb], pw[qb], p.qscale);
+        qf[qb][kk] = __builtin_bit_cast(bf16x8, pk);
+      }
+    // keep Q in AGPRs: the MFMA reads its B operand from there directly and the
+    // arch VGPRs stay free for the scores and the softmax
+    asm volatile(""
+                 : "+a"(qf[0][0]), "+a"(qf[0][1]), "+a"(qf[0][2]), "+a"(qf[0][3]), "+a"(qf[0][4]), "+a"(qf[0][5]),
+                   "+a"(qf[0][6]), "+a"(qf[0][7]), "+a"(qf[1][0]), "+a"(qf[1][1]), "+a"(qf[1][2]), "+a"(qf[1][3]),
+                   "+a"(qf[1][4]), "+a"(qf[1][5]), "+a"(qf[1][6]), "+a"(qf[1][7]));
+
+    floatx16 acc[2][4];
+  #pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+  #pragma unroll
       for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          po[(qb * 16 + 4 * db + g4) * 64] =
-              make_float4(acc[qb][db][4 * g4 + 0], acc[qb][db][4 * g4 + 1], acc[qb][db][4 * g4 + 2],
-                          acc[qb][db][4 * g4 + 3]);
-    }
-    wait_vm<0>();
-    continue;
-  }
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) acc[qb][db][j] = 0.0f;
+    // The O products (phase B below) are inline asm so that their accumulators
+    // live in AGPRs for the whole loop: the arch VGPRs then hold the scores,
+    // the operands and the loop invariants without parking any of them in AGPRs
+    // (which cost ~20 copies per block).  The compiler does not know these asm
+    // statements are MFMAs and inserts no wait states around them, so this fence
+    // does: 24 wait states (more than the 8-pass MFMA's result latency) before
+    // any VALU access of O after an O product, and after VALU writes of O
+    // (initialisation, rescale) before the next product reads them.  Dependent
+    // MFMA -> MFMA accumulation needs none (the hardware interlocks it).
+    auto acc_fence = [&]() __attribute__((always_inline)) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                     "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
+    };
+    acc_fence();
+    // Running softmax reference per query row, kept as a bias b = -m added to the
+    // scores inside the QK^T product: the first k-step of the product starts
+    // from an accumulator tile holding b (every value a lane holds in S^T
+    // belongs to its own query column, so the tile is b repeated).  The scores
+    // come out of the product already shifted, and p = exp2(s) needs no
+    // subtraction; the tile only changes when the reference moves.
+    float bias[2] = {0.0f, 0.0f}, lrun[2] = {0.0f, 0.0f};
+    floatx16 btile[2];
+    auto set_bias = [&](int qb, float b) __attribute__((always_inline)) {
+      bias[qb] = b;
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) btile[qb][e] = b;
+    };
+    set_bias(0, 0.0f);
+    set_bias(1, 0.0f);
 
-  // ---- epilogue: O = O^T / l, bf16.  A lane holds d = 32 db + 8 g4 + 4 hh + 0..3
-  // of one query; each wave writes its 64 rows into LDS (chunks XOR-swizzled
-  // by row) and reads them back as whole 256-byte rows, so that the stores to
-  // O are 16 bytes per lane and 1 KiB (4 full rows) per instruction instead
-  // of 8-byte pieces of 32 rows.  Every wave is past its last LDS operand read
-  // and no tile load is in flight after the barrier.
-  acc_fence();
-  wait_vm<0>();
-  tile_barrier();
-  char* orows = lds + wave * (64 * kRowBytes);
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float inv = 1.0f / wave_half_sum(lrun[qb]);
-    const int row = qb * 32 + r;
-#pragma unroll
+    // LDS operand offsets inside a stage.  K: row r (+32 kb), stored chunk
+    // (2 kk + hh) ^ (r & 15).  V (transposed reads): lane (vg, vu, vq) supplies
+    // key 8 (vg>>1) + vu (+ 32 kb + 16 sl + 4 e) and d 32 db + 16 (vg&1) + 4 vq,
+    // whose chunk 4 db + 2 (vg&1) + vq/2 is stored at 4 (db ^ vu) + 2 (vg&1) + vq/2.
+    int koff[8];
+  #pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      koff[kk] = r * kRowBytes + 16 * ((2 * kk + hh) ^ (r & 15));
+      asm volatile("" : "+v"(koff[kk]));
+    }
+    const int vg = lane >> 4, vu = (lane & 15) >> 2, vq = lane & 3;
+    int voff[4];
+  #pragma unroll
     for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv);
-        w[1] = pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv);
-        *(u32x2*)(orows + row * kRowBytes + 16 * ((4 * db + g4) ^ (row & 15)) + 8 * hh) = w;
+      voff[db] = kVHalves + (8 * (vg >> 1) + vu) * kRowBytes +
+                 16 * (4 * (db ^ vu) + 2 * (vg & 1) + (vq >> 1)) + 8 * (vq & 1);
+  #pragma unroll
+    for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(voff[db]));
+
+    bf16x8 kop[8];      // K' operands of the next block to score
+    bf16x8 vop[4][2];   // V operands of the block being accumulated
+    float sv[2][16];    // scores of the block being finished (base 2, VGPR copy)
+    floatx16 sacc[2];   // MFMA accumulators of the block being scored
+    bf16x8 pcar[2];     // P of keys 0..15 of the block being finished, taken one phase early
+    float scar[2];      // and this lane's sums of them
+
+    auto load_kops = [&](auto S, int kb) __attribute__((always_inline)) {
+      const char* kt = stage(S) + kb * 32 * kRowBytes;
+  #pragma unroll
+      for (int kk = 0; kk < 8; ++kk) kop[kk] = *(const bf16x8*)(kt + koff[kk]);
+    };
+    // single operand reads, for the hand-ordered block step
+    auto load_kop = [&](auto S, int kb, int kk) __attribute__((always_inline)) {
+      kop[kk] = *(const bf16x8*)(stage(S) + kb * 32 * kRowBytes + koff[kk]);
+    };
+    auto load_vop = [&](auto S, int kb, int db, int sl) __attribute__((always_inline)) {
+      const char* vt = stage(S) + kb * 32 * kRowBytes;
+      shortx4 tr[2];
+  #pragma unroll
+      for (int e = 0; e < 2; ++e)
+        tr[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(vt + (16 * sl + 4 * e) * kRowBytes + voff[db]));
+      // whole-vector casts: assembling this operand element by element was
+      // lowered to a splat of element 0 by the compiler
+      vop[db][sl] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, tr[0]), __builtin_bit_cast(bf16x4, tr[1]),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto qk = [&]() __attribute__((always_inline)) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[0][0], btile[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qf[1][0], btile[1], 0, 0, 0);
+  #pragma unroll
+      for (int kk = 1; kk < 8; ++kk) {
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], sacc[1], 0, 0, 0);
       }
-  }
-  const int sr = lane >> 4, sc = lane & 15;
-  const int irow0 = i0 + wave * 64 + sr;
-  uint16_t* dst = p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc;
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int row = 4 * it + sr;
-    const u32x4 w = *(const u32x4*)(orows + row * kRowBytes + 16 * (sc ^ (row & 15)));
-    if (irow0 + 4 * it < p.N) *(u32x4*)dst = w;
-    dst += 4 * row_stride;
-  }
-  if constexpr (!PERSIST) break;
+    };
+    // exp2 of the shifted scores in sv: bf16 operands of the PV product and this
+    // lane's fp32 block sums.  One pair of probabilities (keys 16 sl + 2 e, + 1)
+    // of row block qb: packed word into pk[e], sum into acc2[e & 1].  (Plain adds:
+    // the dot-product VALU instructions wait for the MFMA pipe to drain.)
+    auto exp_pair = [&](int qb, int sl, int e, u32x4& pk, float (&acc2)[2]) __attribute__((always_inline)) {
+      const float p0 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e]);
+      const float p1 = __builtin_amdgcn_exp2f(sv[qb][8 * sl + 2 * e + 1]);
+      // pairs e = 0, 1 start the two partial sums (every caller takes e in
+      // order 0..3): assigning rather than adding to 0 saves an add, which the
+      // compiler may not drop itself (0 + x is not x for x = -0)
+      if (e < 2) acc2[e & 1] = p0 + p1;
+      else acc2[e & 1] += p0 + p1;
+      pk[e] = pack_bf16x2(p0, p1);
+    };
+    // (half sl of the block: keys 16 sl .. 16 sl + 15, registers 8 sl .. 8 sl + 7)
+    auto exp_half = [&](int qb, int sl, bf16x8& out, float& sum) __attribute__((always_inline)) {
+      float acc2[2] = {0.0f, 0.0f};
+      u32x4 pk;
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) exp_pair(qb, sl, e, pk, acc2);
+      out = __builtin_bit_cast(bf16x8, pk);
+      sum = acc2[0] + acc2[1];
+    };
+    auto softmax_exp_row = [&](int qb, bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
+      float h0, h1;
+      exp_half(qb, 0, pb[qb][0], h0);
+      exp_half(qb, 1, pb[qb][1], h1);
+      bsum[qb] = h0 + h1;
+    };
+    // copy the scored block to VGPRs
+    auto take_scores = [&]() __attribute__((always_inline)) {
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) sv[qb][e] = sacc[qb][e];
+    };
+    // visibility of block j: key of register e is 32 j + 16 (e/8) + 8 hh + e%8
+    auto mask_scores = [&](int j) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = 32 * j + 16 * (e >> 3) + 8 * hh + (e & 7);
+          if (key >= lim[qb]) sv[qb][e] = -__builtin_inff();
+        }
+    };
+    auto row_max = [&](int qb) __attribute__((always_inline)) -> float {
+      float m0 = fmaxf(sv[qb][0], sv[qb][1]);
+  #pragma unroll
+      for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(sv[qb][e], sv[qb][e + 1]));
+      return wave_half_max(m0);
+    };
+    // Lazy reference (rare after the first blocks).  The probabilities of block
+    // j were taken against the current reference; when a lane's partial block
+    // sum exceeds kLazySum (some p above 2^12, or an overflow to inf), every row
+    // whose block max lies above its reference moves the reference to that max:
+    // O and l are scaled by 2^(b_new - b_old), block j's probabilities are taken
+    // again, and the scores of block j+1 (already formed against the old
+    // reference) are shifted alike.  One wave-uniform branch for both row blocks.
+    auto move_reference = [&](bf16x8 (&pb)[2][2], float (&bsum)[2]) __attribute__((always_inline)) {
+      acc_fence();
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m = row_max(qb);
+        const float old = bias[qb];
+        set_bias(qb, m > 0.0f ? old - m : old);
+        const float delta = bias[qb] - old;
+        const float alpha = __builtin_amdgcn_exp2f(delta);
+        lrun[qb] *= alpha;
+  #pragma unroll
+        for (int db = 0; db < 4; ++db)
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) acc[qb][db][e] *= alpha;
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sv[qb][e] += delta;
+          sacc[qb][e] += delta;
+        }
+        softmax_exp_row(qb, pb, bsum);
+      }
+      acc_fence();
+      // P was just rewritten by VALU and is read next by the O products
+      asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
+    };
+
+    // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored and
+    // finished, K' operands of block 1 loaded
+    if (nt > 1) wait_vm<8>();
+    else wait_vm<0>();
+    tile_barrier();
+    if (nt > 2) issue_tile(S2{}, 2);
+    load_kops(S0{}, 0);
+    qk();
+    load_kops(S0{}, 1);
+    {
+      // block 0 was scored with b = 0; its row max becomes the first reference
+      // (every row sees key 0, so the max is finite; O and l are still zero)
+      take_scores();
+      if (32 > kv_full) mask_scores(0);
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        set_bias(qb, -row_max(qb));
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) sv[qb][e] += bias[qb];
+        exp_half(qb, 0, pcar[qb], scar[qb]);
+      }
+    }
+
+    // ---- main pipeline.  Block j of tile t (stage S) with j = 2t + kb:
+    //   (first block of a tile: tile t+1 resident, tile t+3 requested)
+    //   A: V operands of block j; S(j+1) = K'(j+1) Q'^T + b  next to  P(j) = exp2(S(j))
+    //      for keys 16..31 and the block sums of P(j)
+    //   (rare, wave-uniform: move the reference, see move_reference)
+    //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
+    //      S(j+1) to VGPRs, its mask (tiles that need one) and P(j+1) for keys 0..15:
+    //      each group is product (row block 0), a pair's exps, product (row block
+    //      1), a K' read, the pair's sum and packing.  One wave issues in order
+    //      and an MFMA leaves the VALU about 4 simple slots: with the two
+    //      products back to back, the first one's slots went unused.
+    // so that both phases carry about the same exp work beside their MFMAs
+    // The step is written as small groups fenced by scheduling barriers, each an
+    // MFMA pair plus the VALU and LDS work meant to run beside it: an MFMA leaves
+    // the VALU only part of its cycles, so that work must be spread evenly.
+    // MASKED steps (the tail loop) check at run time which tiles exist; the
+    // others (the unrolled main loop) only run where tiles t+1..t+3 exist and
+    // t+3 is full, and need no element mask.
+    auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
+      const int j = 2 * t + kb;
+      if constexpr (!decltype(MASKED)::value) {
+        // the loads of tile t+3 are spread over the QK^T groups below
+        if (kb == 0) {
+          wait_vm<8>();
+          tile_barrier();
+        }
+      } else if (kb == 0 && t + 1 < nt) {
+        if (t + 2 < nt) wait_vm<8>();
+        else wait_vm<0>();
+        tile_barrier();
+        if (t + 3 < nt) issue_tile(SNN, t + 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- phase A: S(j+1) = K'(j+1) Q'^T + b; P(j) for keys 16..31; V(j) operands
+      // lgkmcnt(0), as an instruction the compiler accounts for: the K' operands
+      // read during the previous phase are complete here, so no drain is needed
+      // later in this phase, after the V reads below have been issued
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      u32x4 pk1[2];
+      float h1[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+      load_vop(S, kb, 0, 0);
+      load_vop(S, kb, 0, 1);
+  #pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], kk == 0 ? btile[0] : sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[1][kk], kk == 0 ? btile[1] : sacc[1], 0, 0, 0);
+        exp_pair(kk >> 2, 1, kk & 3, pk1[kk >> 2], h1[kk >> 2]);
+        // keep the packed word here: it is only read after the check below,
+        // and would otherwise be sunk past it
+        asm volatile("" : "+v"(pk1[kk >> 2][kk & 3]));
+        if (kk < 6) load_vop(S, kb, 1 + kk / 2, kk & 1);
+        if constexpr (!decltype(MASKED)::value) {
+          if (kb == 0) issue_one(SNN, t + 3, kk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bf16x8 pb[2][2];
+      float bsum[2];
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        pb[qb][0] = pcar[qb];
+        pb[qb][1] = __builtin_bit_cast(bf16x8, pk1[qb]);
+        bsum[qb] = scar[qb] + (h1[qb][0] + h1[qb][1]);
+      }
+      // rare: marked unlikely so that the rescale is placed out of line and the
+      // common path runs on without a taken branch (inline, every block ended in a
+      // jump over it)
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(fmaxf(bsum[0], bsum[1]) > kLazySum) != 0, 0))
+        move_reference(pb, bsum);
+      lrun[0] += bsum[0];
+      lrun[1] += bsum[1];
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- phase B: O += V(j)^T P(j)^T; K'(j+2) operands; S(j+1) to VGPRs (and
+      // its mask); P(j+1) for keys 0..15
+      u32x4 pk0[2];
+      float h0[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+  #pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int db = g >> 1, sl = g & 1;
+        const int qb = g >> 2, e = g & 3;  // the pair (keys 2e, 2e+1 of row block qb) of this group
+        // O^T += V^T P^T with the accumulator in AGPRs (see acc_fence)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[0][db]) : "a"(vop[db][sl]), "v"(pb[0][sl]));
+        if (g == 0) {
+          take_scores();
+          if constexpr (decltype(MASKED)::value) mask_scores(j + 1);
+        }
+        // the exps after this product, not hoisted above it (the two products
+        // of a group would otherwise issue back to back)
+        asm volatile("" : "+v"(sv[qb][2 * e]), "+v"(sv[qb][2 * e + 1]));
+        float p0 = __builtin_amdgcn_exp2f(sv[qb][2 * e]);
+        float p1 = __builtin_amdgcn_exp2f(sv[qb][2 * e + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[1][db]) : "a"(vop[db][sl]), "v"(pb[1][sl]));
+        asm volatile("" : "+v"(p0), "+v"(p1));
+        load_kop(SN, kb, g);
+        if (e < 2) h0[qb][e & 1] = p0 + p1;
+        else h0[qb][e & 1] += p0 + p1;
+        pk0[qb][e] = pack_bf16x2(p0, p1);
+        asm volatile("" : "+v"(pk0[qb][e]), "+v"(h0[qb][e & 1]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        pcar[qb] = __builtin_bit_cast(bf16x8, pk0[qb]);
+        scar[qb] = h0[qb][0] + h0[qb][1];
+      }
+    };
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+    // Block j+1 (scored in step j) needs the element mask iff 32 (j+1) + 32 > kv_full,
+    // i.e. from block jm = kv_full / 32 on.  Whole tiles whose steps score only
+    // earlier blocks, and for which tile t+3 exists and is full, run in the
+    // unrolled loop with compile-time stages; the rest (the last few tiles, or
+    // the chunk a causal query tile straddles) run in a loop with run-time stages.
+    const int jm = kv_full / 32;
+    const int tm = max(0, min(min(nt, (jm - 1) / 2), Nk / kBN - 3));
+    auto tile_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t) __attribute__((always_inline)) {
+      block_step(S, SN, SNN, MASKED, t, 0);
+      block_step(S, SN, SNN, MASKED, t, 1);
+    };
+    // unrolled over 8 tiles (the loop-carried scores and operands then return
+    // to their registers without the copies a 4-tile body needed), then 4
+    int t = 0;
+    for (; t + 8 <= tm; t += 8) {
+      tile_step(S0{}, S1{}, S3{}, NoMask{}, t);
+      tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 1);
+      tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 2);
+      tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 3);
+      tile_step(S0{}, S1{}, S3{}, NoMask{}, t + 4);
+      tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 5);
+      tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 6);
+      tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 7);
+    }
+    for (; t + 4 <= tm; t += 4) {
+      tile_step(S0{}, S1{}, S3{}, NoMask{}, t);
+      tile_step(S1{}, S2{}, S0{}, NoMask{}, t + 1);
+      tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 2);
+      tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 3);
+    }
+    for (; t < nt; ++t) tile_step(t, t + 1, t + 3, Mask{}, t);
+
+    if (split) {
+      // ---- partial epilogue: O, l and the bias as they stand, fp32, one
+      // whole 1 KiB run of float4 per store instruction
+      acc_fence();
+      float4* po = p.part_o + (size_t)item * kPartO + (size_t)(2 * wave) * 16 * 64 + lane;
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float l = wave_half_sum(lrun[qb]);
+        if (hh == 0) p.part_lb[(size_t)item * kBM + (2 * wave + qb) * 32 + r] = make_float2(l, bias[qb]);
+  #pragma unroll
+        for (int db = 0; db < 4; ++db)
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            po[(qb * 16 + 4 * db + g4) * 64] =
+                make_float4(acc[qb][db][4 * g4 + 0], acc[qb][db][4 * g4 + 1], acc[qb][db][4 * g4 + 2],
+                            acc[qb][db][4 * g4 + 3]);
+      }
+      wait_vm<0>();
+      continue;
+    }
+
+    // ---- epilogue: O = O^T / l, bf16.  A lane holds d = 32 db + 8 g4 + 4 hh + 0..3
+    // of one query; each wave writes its 64 rows into LDS (chunks XOR-swizzled
+    // by row) and reads them back as whole 256-byte rows, so that the stores to
+    // O are 16 bytes per lane and 1 KiB (4 full rows) per instruction instead
+    // of 8-byte pieces of 32 rows.  Every wave is past its last LDS operand read
+    // and no tile load is in flight after the barrier.
+    acc_fence();
+    wait_vm<0>();
+    tile_barrier();
+    char* orows = lds + wave * (64 * kRowBytes);
+  #pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float inv = 1.0f / wave_half_sum(lrun[qb]);
+      const int row = qb * 32 + r;
+  #pragma unroll
+      for (int db = 0; db < 4; ++db)
+  #pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv);
+          w[1] = pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv);
+          *(u32x2*)(orows + row * kRowBytes + 16 * ((4 * db + g4) ^ (row & 15)) + 8 * hh) = w;
+        }
+    }
+    const int sr = lane >> 4, sc = lane & 15;
+    const int irow0 = i0 + wave * 64 + sr;
+    uint16_t* dst = p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc;
+  #pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = 4 * it + sr;
+      const u32x4 w = *(const u32x4*)(orows + row * kRowBytes + 16 * (sc ^ (row & 15)));
+      if (irow0 + 4 * it < p.N) *(u32x4*)dst = w;
+      dst += 4 * row_stride;
+    }
+    if constexpr (!PERSIST) break;
   }
 }
 

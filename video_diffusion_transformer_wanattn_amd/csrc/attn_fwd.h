@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     // A persistent pass reads the arguments again from the kernel argument
     // segment (through a pointer the compiler cannot see through) and derives
     // the lane constants again: otherwise they are all kept in registers across
-    // passes (~100 SGPRs and ~80 VGPRs of spills).
+    // passes (70 SGPRs and 37 VGPRs of spills, against 4 and 0).
     const auto& p = [&]() -> decltype(auto) {
       if constexpr (PERSIST) {
         auto kp = (const __attribute__((address_space(4))) AttnParams*)__builtin_amdgcn_kernarg_segment_ptr();

@@ -58,11 +58,11 @@ def split_heads(B, N, heads, n_cu):
     """(batch, head) pairs holding the query tiles that bidirectional self
     attention runs as key-split workgroups on a chip of n_cu compute units
     (with a workspace that has room for the partials): a remainder of at most
-    half the chip, or the last whole wave of 4 or more."""
+    half the chip, or the last whole wave of 12 or more."""
     ntq = (N + 255) // 256
     total = B * heads * ntq
     rem = total % n_cu
-    if rem == 0 and total >= 4 * n_cu:
+    if rem == 0 and total >= 12 * n_cu:
         tail = n_cu
     elif rem and total > n_cu and 2 * rem <= n_cu:
         tail = rem

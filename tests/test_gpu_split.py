@@ -3,7 +3,7 @@ the fp64 oracle.
 
 A launch whose workgroups fill the chip whole times over plus a remainder of
 at most half the chip runs the remainder's query tiles as several workgroups
-each, over ranges of the keys (without remainder, from 4 waves on, the last
+each, over ranges of the keys (without remainder, from 12 waves on, the last
 wave's tiles in two), and combines their partial softmax results (each
 against its own running reference) in a second kernel.  The shapes here
 are chosen from the device's compute-unit count so that the split happens,
@@ -92,11 +92,11 @@ def test_split_tail_with_kv_lens():
 
 
 def test_split_last_whole_wave_in_two():
-    # 4 whole waves of workgroups and no remainder: the last wave runs as 2
-    # key ranges per tile; sampled rows of every tile, all split heads
+    # 12 whole waves of tiles and no remainder: the last wave runs as 2 key
+    # ranges per tile; sampled rows of every tile, all split heads
     grid, N = (5, 20, 20), 2000
     n_cu = ncu()
-    heads = max(1, n_cu // 2)
+    heads = max(1, 12 * n_cu // 8)
     q, k = (gen((1, N, heads, 128), 914, s, 1.0) for s in (1, 2))
     v = gen((1, N, heads, 128), 914, 3, 0.5)
     got = from_dev(wa.self_attention(to_dev(q), to_dev(k), to_dev(v), grid, theta=THETA))

@@ -171,7 +171,9 @@ wanattn_status check_lens(int32_t B, const int32_t* lens, int32_t maxlen, const 
 // writing fp32 partials into the caller's workspace; a small kernel then
 // combines them.  The short workgroups fill the chip as it empties:
 //  - a remainder of at most C / 2 tiles: nsplit = C / remainder (at most 8);
-//  - no remainder, at least 4 waves: the last wave, nsplit = 2.
+//  - no remainder, at least 12 waves: the last wave, nsplit = 2 (the spread
+//    builds up over the waves: at 6 waves the split cost 0.5%, at 20 it gained
+//    0.7%).
 // (Measured inside the persistent launch, 40 heads: 75,600 tokens 81.1 ->
 // 80.8 ms, 32,760 tokens 15.49 -> 15.34 ms.)
 // kSplitItemBytes per split workgroup.
@@ -203,7 +205,7 @@ int choose_split(int total, int ncu, int minlen, size_t room, int* tail_out) {
   if (ncu < 2) return 0;
   const int rem = total % ncu;
   int tail, nsplit;
-  if (rem == 0 && total >= 4 * ncu) {
+  if (rem == 0 && total >= 12 * ncu) {
     tail = ncu;
     nsplit = 2;
   } else if (rem > 0 && total > ncu && 2 * rem <= ncu) {

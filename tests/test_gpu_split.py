@@ -162,3 +162,20 @@ def test_full_size_two_batches_with_kv_lens():
     del o
     ref = oracle.self_rows(q, k, v, grid, rows=rows, theta=THETA, kv_lens=lens)
     assert_parity(got, ref, what="two batches with kv_lens at full size")
+
+
+def test_split_tail_eight_ranges():
+    # 4,320 tokens (17 query tiles, 68 key tiles) x heads so that the launch is
+    # one chip of tiles plus a sixteenth: that remainder runs as 8 key ranges
+    # (the most the library makes) of 8 or 9 key tiles each
+    grid, N = (4, 30, 36), 4320
+    n_cu = ncu()
+    heads = max(1, (n_cu + n_cu // 16) // 17)
+    q, k = (gen((1, N, heads, 128), 916, s, 1.0) for s in (1, 2))
+    v = gen((1, N, heads, 128), 916, 3, 0.5)
+    got = from_dev(wa.self_attention(to_dev(q), to_dev(k), to_dev(v), grid, theta=THETA))
+    torch.cuda.synchronize()
+    hs = np.array(sorted({h for _, h in split_heads(1, N, heads, n_cu)} | {0}))
+    rows = seeded.sample_rows(N, 96, seed=916, must=tuple(256 * t for t in range(17)) + (N - 1,))
+    ref = oracle.self_rows(q[:, :, hs], k[:, :, hs], v[:, :, hs], grid, rows=rows, theta=THETA)
+    assert_parity(got[:, rows][:, :, hs], ref, what="split tail, 8 ranges")

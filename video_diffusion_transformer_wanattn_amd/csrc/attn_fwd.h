@@ -11,10 +11,14 @@
 // long-video survey (atlascloud.ai) puts it at ~10 GB for 32.7k tokens).
 //
 // Work decomposition
-//   one workgroup = 4 waves = 256 query rows of one (batch, head); a wave owns
+//   one work item = 4 waves = 256 query rows of one (batch, head); a wave owns
 //   64 rows as two 32-row MFMA blocks.  Keys stream through LDS in tiles of 64
 //   (K' 16 KiB + V 16 KiB), 4 stages, filled with global_load_lds_dwordx4 (no
 //   staging registers), two tiles in flight ahead of the one being computed.
+//   A plain launch runs one item per workgroup; a persistent launch runs one
+//   workgroup per compute unit that draws items from per-XCD queues (XCDs run
+//   at different speeds), the last items being key ranges of the last query
+//   tiles, whose partial results split_merge_kernel combines.
 //
 // Per 32-key block and wave (two blocks per tile):
 //   S^T (keys x queries) = K' Q'^T   v_mfma_f32_32x32x16_bf16, 2 x 8 issues

@@ -599,9 +599,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
     //      S(j+1) to VGPRs, its mask (tiles that need one) and P(j+1) for keys 0..15:
     //      each group is product (row block 0), a pair's exps, product (row block
-    //      1), a K' read, the pair's sum and packing.  One wave issues in order
-    //      and an MFMA leaves the VALU about 4 simple slots: with the two
-    //      products back to back, the first one's slots went unused.
+    //      1), a K' read, the previous pair's sum and packing (one group after
+    //      its exps, clear of their latency).  One wave issues in order and an
+    //      MFMA leaves the VALU about 4 simple slots: with the two products back
+    //      to back, the first one's slots went unused.
     // so that both phases carry about the same exp work beside their MFMAs
     // The step is written as small groups fenced by scheduling barriers, each an
     // MFMA pair plus the VALU and LDS work meant to run beside it: an MFMA leaves
@@ -667,6 +668,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
       // its mask); P(j+1) for keys 0..15
       u32x4 pk0[2];
       float h0[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+      float lag0 = 0.0f, lag1 = 0.0f;  // the previous group's pair, summed and packed one group later
+      auto finish_pair = [&](int gp, float a0, float a1) __attribute__((always_inline)) {
+        const int qb = gp >> 2, e = gp & 3;
+        if (e < 2) h0[qb][e & 1] = a0 + a1;
+        else h0[qb][e & 1] += a0 + a1;
+        pk0[qb][e] = pack_bf16x2(a0, a1);
+        asm volatile("" : "+v"(pk0[qb][e]), "+v"(h0[qb][e & 1]));
+      };
   #pragma unroll
       for (int g = 0; g < 8; ++g) {
         const int db = g >> 1, sl = g & 1;
@@ -680,18 +689,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         // the exps after this product, not hoisted above it (the two products
         // of a group would otherwise issue back to back)
         asm volatile("" : "+v"(sv[qb][2 * e]), "+v"(sv[qb][2 * e + 1]));
-        float p0 = __builtin_amdgcn_exp2f(sv[qb][2 * e]);
-        float p1 = __builtin_amdgcn_exp2f(sv[qb][2 * e + 1]);
+        const float p0 = __builtin_amdgcn_exp2f(sv[qb][2 * e]);
+        const float p1 = __builtin_amdgcn_exp2f(sv[qb][2 * e + 1]);
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[1][db]) : "a"(vop[db][sl]), "v"(pb[1][sl]));
-        asm volatile("" : "+v"(p0), "+v"(p1));
+        asm volatile("" : "+v"(lag0), "+v"(lag1));
         load_kop(SN, kb, g);
-        if (e < 2) h0[qb][e & 1] = p0 + p1;
-        else h0[qb][e & 1] += p0 + p1;
-        pk0[qb][e] = pack_bf16x2(p0, p1);
-        asm volatile("" : "+v"(pk0[qb][e]), "+v"(h0[qb][e & 1]));
+        if (g > 0) finish_pair(g - 1, lag0, lag1);
+        lag0 = p0;
+        lag1 = p1;
         __builtin_amdgcn_sched_barrier(0);
       }
+      finish_pair(7, lag0, lag1);
   #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         pcar[qb] = __builtin_bit_cast(bf16x8, pk0[qb]);

@@ -599,10 +599,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     //   B: O += V(j)^T P(j)^T  next to  K' operands of block j+2, the copy of
     //      S(j+1) to VGPRs, its mask (tiles that need one) and P(j+1) for keys 0..15:
     //      each group is product (row block 0), a pair's exps, product (row block
-    //      1), a K' read, the previous pair's sum and packing (one group after
-    //      its exps, clear of their latency).  One wave issues in order and an
-    //      MFMA leaves the VALU about 4 simple slots: with the two products back
-    //      to back, the first one's slots went unused.
+    //      1), the previous pair's sum and packing (one group after its exps,
+    //      clear of their latency); groups 0..3 also read two K' operands each,
+    //      so that the wait for them at the start of phase A finds them done.
+    //      One wave issues in order and an MFMA leaves the VALU about 4 simple
+    //      slots: with the two products back to back, the first one's slots
+    //      went unused.
     // so that both phases carry about the same exp work beside their MFMAs
     // The step is written as small groups fenced by scheduling barriers, each an
     // MFMA pair plus the VALU and LDS work meant to run beside it: an MFMA leaves
@@ -694,7 +696,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[1][db]) : "a"(vop[db][sl]), "v"(pb[1][sl]));
         asm volatile("" : "+v"(lag0), "+v"(lag1));
-        load_kop(SN, kb, g);
+        if (g < 4) {
+          load_kop(SN, kb, 2 * g);
+          load_kop(SN, kb, 2 * g + 1);
+        }
         if (g > 0) finish_pair(g - 1, lag0, lag1);
         lag0 = p0;
         lag1 = p1;

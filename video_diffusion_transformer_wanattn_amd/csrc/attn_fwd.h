@@ -634,8 +634,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
       __builtin_amdgcn_s_waitcnt(0xC07F);
       u32x4 pk1[2];
       float h1[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-      load_vop(S, kb, 0, 0);
-      load_vop(S, kb, 0, 1);
   #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], kk == 0 ? btile[0] : sacc[0], 0, 0, 0);
@@ -644,7 +642,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         // keep the packed word here: it is only read after the check below,
         // and would otherwise be sunk past it
         asm volatile("" : "+v"(pk1[kk >> 2][kk & 3]));
-        if (kk < 6) load_vop(S, kb, 1 + kk / 2, kk & 1);
+        load_vop(S, kb, kk >> 1, kk & 1);
         if constexpr (!decltype(MASKED)::value) {
           if (kb == 0) issue_one(SNN, t + 3, kk);
         }

@@ -499,7 +499,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     };
     // (half sl of the block: keys 16 sl .. 16 sl + 15, registers 8 sl .. 8 sl + 7)
     auto exp_half = [&](int qb, int sl, bf16x8& out, float& sum) __attribute__((always_inline)) {
-      float acc2[2] = {0.0f, 0.0f};
+      float acc2[2];
       u32x4 pk;
   #pragma unroll
       for (int e = 0; e < 4; ++e) exp_pair(qb, sl, e, pk, acc2);
@@ -633,7 +633,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
       // later in this phase, after the V reads below have been issued
       __builtin_amdgcn_s_waitcnt(0xC07F);
       u32x4 pk1[2];
-      float h1[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+      float h1[2][2];  // set by pairs 0 and 1, added to by 2 and 3
   #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[0][kk], kk == 0 ? btile[0] : sacc[0], 0, 0, 0);
@@ -667,8 +667,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
       // ---- phase B: O += V(j)^T P(j)^T; K'(j+2) operands; S(j+1) to VGPRs (and
       // its mask); P(j+1) for keys 0..15
       u32x4 pk0[2];
-      float h0[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-      float lag0 = 0.0f, lag1 = 0.0f;  // the previous group's pair, summed and packed one group later
+      float h0[2][2];  // set by pairs 0 and 1, added to by 2 and 3
+      float lag0, lag1;  // the previous group's pair, summed and packed one group later
       auto finish_pair = [&](int gp, float a0, float a1) __attribute__((always_inline)) {
         const int qb = gp >> 2, e = gp & 3;
         if (e < 2) h0[qb][e & 1] = a0 + a1;
@@ -693,7 +693,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         const float p1 = __builtin_amdgcn_exp2f(sv[qb][2 * e + 1]);
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[1][db]) : "a"(vop[db][sl]), "v"(pb[1][sl]));
-        asm volatile("" : "+v"(lag0), "+v"(lag1));
+        if (g > 0) asm volatile("" : "+v"(lag0), "+v"(lag1));
         if (g < 4) {
           load_kop(SN, kb, 2 * g);
           load_kop(SN, kb, 2 * g + 1);

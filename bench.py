@@ -338,7 +338,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the attention kernels run on one device; "
-              "multi-GPU sharding (heads over GPUs) is described in DESIGN.md and not built",
+              "sharding heads over several GPUs is not implemented; run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 

@@ -328,3 +328,14 @@ def test_binding_refuses_host_tensors():
     e = torch.zeros(1, 256)
     with pytest.raises(ValueError):
         wa.prologue(y, e, e, w, b, w, b, w, b, b, b, out=(y, y, y))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one device; asked for more it exits before any GPU work
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""

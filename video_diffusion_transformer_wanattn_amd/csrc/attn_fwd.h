@@ -176,10 +176,10 @@ __device__ __forceinline__ void tile_barrier() {
 
 // 16 bytes per lane from gbase + voff into LDS at lds + 16 * lane.  Written as
 // asm so that the compiler does not track the LDS write (the kernel waits for
-// these loads itself with vmcnt and a barrier)
+// these loads itself with vmcnt and a barrier).  The LDS address is an m0
+// operand: the compiler writes m0 itself and knows it is in use.
 __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
 }
 
 template <bool ROPE, bool CAUSAL, bool PERSIST = false>

@@ -31,8 +31,12 @@
  *    column; frequency k of an axis of width D is theta^(-2k/D).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    work and return; success means "enqueued".  Nothing synchronises the
- *    device, except the first use of a new theta on a device (see
- *    wanattn_prepare).
+ *    host with the device (wanattn_prepare and the prologue's first call on a
+ *    device aside).  The rotary table of a theta ([P1] builds `freqs` once,
+ *    at construction) is built on the device, in fp64 rounded to fp32, by the
+ *    first call that uses that theta on a device, on that call's stream;
+ *    calls on other streams wait for it through an event, and a call under
+ *    HIP stream capture puts its own build of the table into the graph.
  *  - Errors: arguments are checked before anything is launched.
  *    WANATTN_E_INVALID: null or misaligned pointer, sizes < 1, N != F*H*W,
  *    positions reaching 1024, an output overlapping an input, bad lengths.
@@ -80,7 +84,7 @@ typedef enum wanattn_mask {
  * [P1] ch. 4, 3D RoPE (rope_apply): y = x rotated by the 3D rotary embedding.
  * x, y: [B, N, heads, 128] bf16; y may equal x (in place) but must not
  * otherwise overlap it.  The rotation is done in fp32 from a table built in
- * fp64 on the host, and rounded to bf16 (nearest even).
+ * fp64 (rounded to fp32), and rounded to bf16 (nearest even).
  */
 wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
                               int32_t head_dim, const wanattn_grid3d* grid, double theta,
@@ -257,10 +261,10 @@ wanattn_status wanattn_prologue(const void* x, const float* e0, const float* e1,
 size_t wanattn_prologue_workspace_bytes(int32_t B, int32_t N, int32_t dim);
 
 /*
- * Build and upload the rotary table for theta on the current device now
- * (a blocking copy).  Otherwise this happens at the first call that uses
- * theta on a device; call it before capturing such calls in a HIP graph.
- * Up to 8 distinct theta values are kept per device.
+ * Build the rotary table for theta on the current device now and wait for it
+ * (a blocking call on the null stream).  Optional: the first call that uses
+ * theta builds it otherwise.  Up to 8 distinct theta values are kept per
+ * device.
  */
 wanattn_status wanattn_prepare(double theta);
 

@@ -9,9 +9,12 @@ G1 is the stated bar; at large N it is nearly vacuous (outputs shrink like
 bf16 kernel lands near 3e-3, one that ignores the scores or the rotation
 near 0.3.
 """
+import math
+
 import numpy as np
 import torch
 
+import oracle
 from video_diffusion_transformer_wanattn_amd import seeded
 
 MAX_ABS = 2e-2
@@ -70,3 +73,21 @@ def split_heads(B, N, heads, n_cu):
         tail = 0
     bhs = sorted({L // ntq for L in range(total - tail, total)})
     return [(bh // heads, bh % heads) for bh in bhs]
+
+
+def plant_needles(q, k, grid, pairs, target=16.0, theta=10000.0):
+    """Set k_j = c R(p_j)^-1 R(p_i) q_i (batch 0, every head) so that the
+    scaled score (q'_i . k'_j) / sqrt(128) is ``target``: row i then takes
+    nearly all its weight from key j, which checks the RoPE positions of both
+    tokens end to end (scores depend only on the coordinate difference)."""
+    F, H, W = grid
+    k = k.copy()
+    for i, j in pairs:
+        pi = oracle.decode(int(i), H, W)
+        pj = oracle.decode(int(j), H, W)
+        for h in range(q.shape[2]):
+            qi = widen(q[0, i, h])
+            rot = oracle.rope_vec(oracle.rope_vec(qi, pi, theta), tuple(-x for x in pj), theta)
+            kj = rot * (target * math.sqrt(128) / (qi @ qi))
+            k[0, j, h] = seeded.f32_to_bf16_bits_array(kj.astype(np.float32))
+    return k

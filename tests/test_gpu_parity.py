@@ -5,14 +5,13 @@ Small shapes are compared on every row and span several 256-row query tiles
 and 64-key tiles with ragged tails; the five workload shapes run at full size
 in the launch configuration the benchmark times, compared on sampled rows.
 """
-import math
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from parity_util import assert_parity, from_dev, to_dev, widen
+from parity_util import assert_parity, from_dev, plant_needles, to_dev, widen
 from video_diffusion_transformer_wanattn_amd import seeded
 from video_diffusion_transformer_wanattn_amd import wanattn as wa
 
@@ -123,21 +122,6 @@ def test_peaked_scores(grid):
                   what=f"peaked {grid}")
     kc, vc = gen((1, 77, 2, 128), 301, 4, 1.5), gen((1, 77, 2, 128), 301, 5)
     assert_parity(gpu_cross(q, kc, vc), oracle.cross_rows(q, kc, vc), what="peaked cross")
-
-
-def plant_needles(q, k, grid, pairs, target=16.0):
-    """Set k_j = c R(p_j)^-1 R(p_i) q_i so that (q'_i . k'_j) / sqrt(128) = target."""
-    F, H, W = grid
-    k = k.copy()
-    for i, j in pairs:
-        pi = oracle.decode(i, H, W)
-        pj = oracle.decode(j, H, W)
-        for h in range(q.shape[2]):
-            qi = widen(q[0, i, h])
-            rot = oracle.rope_vec(oracle.rope_vec(qi, pi, THETA), tuple(-x for x in pj), THETA)
-            kj = rot * (target * math.sqrt(128) / (qi @ qi))
-            k[0, j, h] = seeded.f32_to_bf16_bits_array(kj.astype(np.float32))
-    return k
 
 
 def test_planted_needles_check_rope_positions():

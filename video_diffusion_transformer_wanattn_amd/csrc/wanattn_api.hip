@@ -17,6 +17,13 @@
 
 using namespace wanattn;
 
+#define WA_TRY(x)                        \
+  do {                                   \
+    wanattn_status st_ = (x);            \
+    if (st_ != WANATTN_OK) return st_;   \
+  } while (0)
+
+
 namespace {
 
 constexpr int kSlots = 8;       // distinct theta values kept per device
@@ -25,13 +32,22 @@ constexpr int kMaxDevices = 64;
 // Rotary tables, one per theta slot, resident on every device the library runs on.
 __device__ float2 g_rope_tab[kSlots][kTabEntries];
 
-struct DeviceTables {
-  bool have_base = false;
-  float2* base = nullptr;          // device address of g_rope_tab on this device
+// Per-device state, set up once per device by the first call that runs there
+// (device_state): the device addresses of the module-scope arrays and one
+// event per theta slot.  A slot's table is built by rope_table_kernel on the
+// stream of the first call that uses its theta; the event recorded after that
+// build lets calls on other streams wait for it.
+struct DeviceState {
+  bool ready = false;
+  float2* tab = nullptr;                 // g_rope_tab on this device
   double theta[kSlots];
+  bool built[kSlots];                    // an eager build of the slot was enqueued ...
+  hipStream_t built_on[kSlots];          // ... on this stream,
+  hipEvent_t ev[kSlots];                 // followed by this event
+  bool done[kSlots];                     // the event has completed
   int used = 0;
 };
-DeviceTables g_dev[kMaxDevices];
+DeviceState g_dev[kMaxDevices];
 std::mutex g_mu;
 
 thread_local char t_err[512] = "";
@@ -45,49 +61,88 @@ wanattn_status fail(wanattn_status s, const char* fmt, ...) {
   return s;
 }
 
-// Host-side table: (cos, sin) of pos * theta^(-2k/D) in fp64, stored as fp32,
-// for the time (D = 44), height (42) and width (42) segments of a 128-wide head.
-void build_table(double theta, float2* tab) {
-  const int widths[3] = {kHeadDim - 4 * (kHeadDim / 6), 2 * (kHeadDim / 6), 2 * (kHeadDim / 6)};
-  memset(tab, 0, sizeof(float2) * kTabEntries);
-  for (int a = 0; a < 3; ++a)
-    for (int k = 0; k < widths[a] / 2; ++k) {
-      const double w = std::pow(theta, -2.0 * k / widths[a]);
-      for (int pos = 0; pos < kMaxPos; ++pos) {
-        const double ang = pos * w;
-        tab[(a * kMaxPos + pos) * kTabStride + k] = make_float2((float)std::cos(ang), (float)std::sin(ang));
-      }
-    }
-}
-
-// Device address of the table for theta on the current device (uploaded on first use).
-wanattn_status table_for(double theta, const float2** out) {
+// the current device's state, set up on first use (caller holds g_mu)
+wanattn_status device_state(DeviceState** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(WANATTN_E_HIP, "hipGetDevice failed");
   if (dev < 0 || dev >= kMaxDevices) return fail(WANATTN_E_UNSUPPORTED, "device %d out of range", dev);
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceTables& d = g_dev[dev];
-  if (!d.have_base) {
+  DeviceState& d = g_dev[dev];
+  if (!d.ready) {
     void* ptr = nullptr;
     hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_rope_tab));
-    if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
-    d.base = (float2*)ptr;
-    d.have_base = true;
-  }
-  for (int s = 0; s < d.used; ++s)
-    if (d.theta[s] == theta) {
-      *out = d.base + (size_t)s * kTabEntries;
-      return WANATTN_OK;
+    if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipGetSymbolAddress(rotary tables): %s", hipGetErrorString(e));
+    d.tab = (float2*)ptr;
+    for (int s = 0; s < kSlots; ++s) {
+      e = hipEventCreateWithFlags(&d.ev[s], hipEventDisableTiming);
+      if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+      d.built[s] = d.done[s] = false;
+      d.built_on[s] = nullptr;
     }
-  if (d.used == kSlots)
-    return fail(WANATTN_E_UNSUPPORTED, "more than %d distinct theta values on device %d", kSlots, dev);
-  static float2 host[kTabEntries];
-  build_table(theta, host);
-  float2* dst = d.base + (size_t)d.used * kTabEntries;
-  hipError_t e = hipMemcpy(dst, host, sizeof(float2) * kTabEntries, hipMemcpyHostToDevice);
-  if (e != hipSuccess) return fail(WANATTN_E_HIP, "table upload: %s", hipGetErrorString(e));
-  d.theta[d.used++] = theta;
-  *out = dst;
+    d.ready = true;
+  }
+  *out = &d;
+  return WANATTN_OK;
+}
+
+// rope_table_kernel for one theta into one slot, on `stream`
+wanattn_status launch_table(double theta, float2* tab, hipStream_t stream) {
+  TableParams tp;
+  memset(&tp, 0, sizeof tp);
+  tp.tab = tab;
+  tp.heads = 1;
+  tp.theta[0] = theta;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(kTabEntries / 256), dim3(256), 0, stream, tp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(WANATTN_E_HIP, "rope_table launch: %s", hipGetErrorString(e));
+  return WANATTN_OK;
+}
+
+// Device address of the table for theta on the current device, ready for
+// work enqueued on `stream` after this call.  The first use of a theta on a
+// device builds its slot on `stream` (the same fp64 formula as the per-head
+// tables of the jitter calls); a later use on another stream waits for that
+// build's event until it is known to have completed.  Under stream capture
+// the graph gets its own build of the slot (identical values) instead of a
+// dependency on work outside the graph, and an eager call later builds the
+// slot again.  Nothing here blocks the host.
+wanattn_status table_for(double theta, hipStream_t stream, const float2** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState* dp = nullptr;
+  WA_TRY(device_state(&dp));
+  DeviceState& d = *dp;
+  int s = 0;
+  while (s < d.used && d.theta[s] != theta) ++s;
+  if (s == d.used) {
+    if (d.used == kSlots) return fail(WANATTN_E_UNSUPPORTED, "more than %d distinct theta values on one device", kSlots);
+    d.theta[s] = theta;
+    d.built[s] = d.done[s] = false;
+    ++d.used;
+  }
+  float2* tab = d.tab + (size_t)s * kTabEntries;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+  if (cap != hipStreamCaptureStatusNone) {
+    // the graph builds the slot itself unless an eager build is known complete
+    if (!d.built[s] || !d.done[s]) WA_TRY(launch_table(theta, tab, stream));
+  } else if (!d.built[s]) {
+    WA_TRY(launch_table(theta, tab, stream));
+    e = hipEventRecord(d.ev[s], stream);
+    if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    d.built[s] = true;
+    d.built_on[s] = stream;
+  } else if (!d.done[s]) {
+    e = hipEventQuery(d.ev[s]);
+    if (e == hipSuccess) {
+      d.done[s] = true;
+    } else if (e != hipErrorNotReady) {
+      return fail(WANATTN_E_HIP, "hipEventQuery: %s", hipGetErrorString(e));
+    } else if (stream != d.built_on[s]) {
+      e = hipStreamWaitEvent(stream, d.ev[s], 0);
+      if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipStreamWaitEvent: %s", hipGetErrorString(e));
+    }
+  }
+  *out = tab;
   return WANATTN_OK;
 }
 
@@ -140,12 +195,6 @@ wanattn_status launched(const char* what) {
   if (e != hipSuccess) return fail(WANATTN_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
   return WANATTN_OK;
 }
-
-#define WA_TRY(x)                        \
-  do {                                   \
-    wanattn_status st_ = (x);            \
-    if (st_ != WANATTN_OK) return st_;   \
-  } while (0)
 
 wanattn_status check_lens(int32_t B, const int32_t* lens, int32_t maxlen, const char* name) {
   if (!lens) return WANATTN_OK;
@@ -312,17 +361,16 @@ wanattn_status rope3d_checked(const void* x, void* y, int32_t B, int32_t N, int3
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
   if (x != y && overlap(x, bytes, y, bytes)) return fail(WANATTN_E_INVALID, "y partially overlaps x");
   const float2* tab = nullptr;
-  WA_TRY(table_for(theta, &tab));
+  WA_TRY(table_for(theta, stream, &tab));
   return rope3d_launch(x, y, B, N, heads, grid, tab, 0, stream);
 }
 
 // argument checks shared by the self-attention entry points (theta checked by
 // the caller); the workspace must hold ws_need bytes, of which the call uses
 // ws_use (ws_need, or more where the tail split's partials fit)
-wanattn_status check_self(const void* q, const void* k, const void* v, const void* o, int32_t B, int32_t N,
-                          int32_t heads, int32_t head_dim, const wanattn_grid3d* grid, float scale,
-                          wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
-                          const void* workspace, size_t workspace_bytes, size_t ws_need, size_t ws_use) {
+wanattn_status check_self_args(const void* q, const void* k, const void* v, const void* o, int32_t B, int32_t N,
+                               int32_t heads, int32_t head_dim, const wanattn_grid3d* grid, float scale,
+                               wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens) {
   if (!q || !k || !v || !o) return fail(WANATTN_E_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
@@ -337,6 +385,16 @@ wanattn_status check_self(const void* q, const void* k, const void* v, const voi
   const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
   if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
     return fail(WANATTN_E_INVALID, "o overlaps an input");
+  return check_lens(B, kv_lens, N, "kv_lens");
+}
+
+// ... and of the caller's workspace
+wanattn_status check_self(const void* q, const void* k, const void* v, const void* o, int32_t B, int32_t N,
+                          int32_t heads, int32_t head_dim, const wanattn_grid3d* grid, float scale,
+                          wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                          const void* workspace, size_t workspace_bytes, size_t ws_need, size_t ws_use) {
+  WA_TRY(check_self_args(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens));
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
   if (!workspace) return fail(WANATTN_E_INVALID, "workspace is NULL");
   if (!aligned16(workspace)) return fail(WANATTN_E_INVALID, "workspace must be 16-byte aligned");
   if (workspace_bytes < ws_need)
@@ -344,7 +402,7 @@ wanattn_status check_self(const void* q, const void* k, const void* v, const voi
   if (overlap(workspace, ws_use, q, bytes) || overlap(workspace, ws_use, k, bytes) ||
       overlap(workspace, ws_use, v, bytes) || overlap(workspace, ws_use, o, bytes))
     return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
-  return check_lens(B, kv_lens, N, "kv_lens");
+  return WANATTN_OK;
 }
 
 // keys rotated once into kprime (with head h's table at tab + h * hstride);
@@ -592,9 +650,13 @@ const char* wanattn_last_error(void) { return t_err; }
 int32_t wanattn_version(void) { return WANATTN_VERSION; }
 
 wanattn_status wanattn_prepare(double theta) {
+  t_err[0] = 0;
   WA_TRY(check_theta(theta));
   const float2* tab = nullptr;
-  return table_for(theta, &tab);
+  WA_TRY(table_for(theta, nullptr, &tab));
+  const hipError_t e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  return WANATTN_OK;
 }
 
 wanattn_status wanattn_rope3d(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
@@ -621,7 +683,7 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
   WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
                     workspace_bytes, bytes, room ? full : bytes));
   const float2* tab = nullptr;
-  WA_TRY(table_for(theta, &tab));
+  WA_TRY(table_for(theta, (hipStream_t)stream, &tab));
   return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens, workspace, tab, 0,
                      room ? (char*)workspace + bytes : nullptr, room ? items : 0, (hipStream_t)stream);
 }
@@ -660,7 +722,7 @@ wanattn_status wanattn_self_kv(const void* q, const void* k_cache, const void* v
   WA_TRY(check_kv(q, k_cache, v_cache, o, B, Nq, Nkv, heads, head_dim, grid_q, scale, kv_lens));
   WA_TRY(check_theta(theta));
   const float2* tab = nullptr;
-  WA_TRY(table_for(theta, &tab));
+  WA_TRY(table_for(theta, (hipStream_t)stream, &tab));
   return kv_launch(q, k_cache, v_cache, o, B, Nq, Nkv, heads, grid_q, tab, 0, scale, kv_lens,
                    (hipStream_t)stream);
 }

@@ -108,6 +108,15 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context in which torch allocates the tensors a call on ``stream`` uses
+    (outputs, workspaces): their memory then belongs to that stream's pool and
+    is only handed out again after the work enqueued there."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -156,7 +165,8 @@ def rope_tables(theta_per_head, out=None, stream=None):
     heads = len(th)
     need = int(lib.wanattn_rope_tables_bytes(heads))
     if out is None:
-        out = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        with _on(stream):
+            out = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     ptr, nbytes = _tables(out)
     _raise_on(lib.wanattn_rope_tables((ctypes.c_double * max(heads, 1))(*th), heads, ptr, nbytes,
                                       _stream(stream)))
@@ -169,7 +179,8 @@ def rope3d(x, grid, theta: float = 10000.0, offsets=(0, 0, 0), out=None, stream=
     import torch
     lib = load_library()
     if out is None:
-        out = torch.empty_like(x)
+        with _on(stream):
+            out = torch.empty_like(x)
     B, N, heads, d = _dims(x, out)
     if tuple(out.shape) != tuple(x.shape):
         raise ValueError("out must have the shape of x")
@@ -207,7 +218,8 @@ def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = 
     import torch
     lib = load_library()
     if out is None:
-        out = torch.empty_like(q)
+        with _on(stream):
+            out = torch.empty_like(q)
     B, N, heads, d = _dims(q, k, v, out)
     if not (tuple(k.shape) == tuple(v.shape) == tuple(out.shape) == tuple(q.shape)):
         raise ValueError("q, k, v and out must have the same shape")
@@ -228,7 +240,9 @@ def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = 
     else:
         need = int(lib.wanattn_self_workspace_bytes(B, N, heads, d))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        # on the launch stream's pool: the kernels still read it after this returns
+        with _on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -253,7 +267,8 @@ def self_attention_kv(q, k_cache, v_cache, grid_q, theta: float = 10000.0, scale
     import torch
     lib = load_library()
     if out is None:
-        out = torch.empty_like(q)
+        with _on(stream):
+            out = torch.empty_like(q)
     B, Nq, heads, d = _dims(q, k_cache, v_cache, out)
     Nkv = int(k_cache.shape[1])
     if tuple(k_cache.shape) != (B, Nkv, heads, d) or tuple(v_cache.shape) != (B, Nkv, heads, d):
@@ -283,7 +298,8 @@ def cross_attention(q, k_ctx, v_ctx, scale: float | None = None, ctx_lens=None, 
     import torch
     lib = load_library()
     if out is None:
-        out = torch.empty_like(q)
+        with _on(stream):
+            out = torch.empty_like(q)
     B, N, heads, d = _dims(q, k_ctx, v_ctx, out)
     M = int(k_ctx.shape[1])
     if tuple(k_ctx.shape) != (B, M, heads, d) or tuple(v_ctx.shape) != (B, M, heads, d):
@@ -320,7 +336,8 @@ def prologue(x, e0, e1, wq, bq, wk, bk, wv, bv, gq, gk, eps_ln: float = 1e-6, ep
         raise ValueError("x must be [B, N, dim]")
     B, N, dim = (int(a) for a in x.shape)
     if out is None:
-        out = tuple(torch.empty_like(x) for _ in range(3))
+        with _on(stream):
+            out = tuple(torch.empty_like(x) for _ in range(3))
     mats, vecs = (wq, wk, wv), (bq, bk, bv, gq, gk)
     for t in (x, *out, *mats, *vecs):
         if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
@@ -336,7 +353,8 @@ def prologue(x, e0, e1, wq, bq, wk, bk, wv, bv, gq, gk, eps_ln: float = 1e-6, ep
         raise ValueError("weights must be [dim, dim] and biases/gammas [dim]")
     need = int(lib.wanattn_prologue_workspace_bytes(B, N, dim))
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+        with _on(stream):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()

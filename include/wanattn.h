@@ -134,6 +134,39 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
  * included (0 for invalid sizes) */
 size_t wanattn_self_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim);
 
+/* Bytes of scratch memory the library holds on every device it runs on, for
+ * wanattn_self_noalloc (512 MiB). */
+#define WANATTN_NOALLOC_SCRATCH_BYTES ((size_t)512 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * wanattn_self without a workspace argument.  Its scratch memory (the rotated
+ * keys, then the key-split partials where they fit, then the work-queue
+ * counters) is a module-scope device array of WANATTN_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each device until the process ends; the call
+ * allocates nothing.  Arguments, errors and numerics as wanattn_self, plus:
+ *  - WANATTN_E_UNSUPPORTED when the rotated keys and the queue counters,
+ *    B * N * heads * head_dim * 2 + 256 bytes, exceed the scratch (e.g.
+ *    32,760 tokens x 40 heads fit, 75,600 x 40 do not); larger calls need
+ *    wanattn_self and a caller workspace;
+ *  - where the split's partials also fit, the results are bitwise those of
+ *    wanattn_self with a full workspace; otherwise those of a workspace
+ *    without room for the split (persistent launch, no split);
+ *  - every call on a device uses that device's one scratch array: calls that
+ *    may overlap on one device (different streams, or captured graphs
+ *    replayed concurrently) race and give wrong results.  Serialise them.
+ *    The queue counters are cleared by a kernel on every call.
+ * The first call on a device sets up the library's per-device state (array
+ * addresses, events) and, as for every entry point, the first use of a theta
+ * enqueues the build of its rotary table on `stream`.
+ */
+wanattn_status wanattn_self_noalloc(const void* q, const void* k, const void* v, void* o, int32_t B,
+                                    int32_t N, int32_t heads, int32_t head_dim,
+                                    const wanattn_grid3d* grid, double theta, float scale,
+                                    wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                                    void* stream);
+
 #define WANATTN_MAX_JITTER_HEADS 256
 
 /*

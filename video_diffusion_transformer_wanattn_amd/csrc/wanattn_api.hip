@@ -32,6 +32,17 @@ constexpr int kMaxDevices = 64;
 // Rotary tables, one per theta slot, resident on every device the library runs on.
 __device__ float2 g_rope_tab[kSlots][kTabEntries];
 
+}  // namespace
+
+// Scratch memory of wanattn_self_noalloc: the rotated keys, the key-split
+// partials and the work-queue counters of one call, for callers that cannot
+// allocate.  Every device the library runs on holds its own copy until the
+// process ends; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device (DeviceState::scratch).
+static __device__ __align__(256) unsigned char scratch[WANATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
 // Per-device state, set up once per device by the first call that runs there
 // (device_state): the device addresses of the module-scope arrays and one
 // event per theta slot.  A slot's table is built by rope_table_kernel on the
@@ -40,6 +51,7 @@ __device__ float2 g_rope_tab[kSlots][kTabEntries];
 struct DeviceState {
   bool ready = false;
   float2* tab = nullptr;                 // g_rope_tab on this device
+  unsigned char* scratch = nullptr;      // scratch on this device
   double theta[kSlots];
   bool built[kSlots];                    // an eager build of the slot was enqueued ...
   hipStream_t built_on[kSlots];          // ... on this stream,
@@ -72,6 +84,10 @@ wanattn_status device_state(DeviceState** out) {
     hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_rope_tab));
     if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipGetSymbolAddress(rotary tables): %s", hipGetErrorString(e));
     d.tab = (float2*)ptr;
+    ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    d.scratch = (unsigned char*)ptr;
     for (int s = 0; s < kSlots; ++s) {
       e = hipEventCreateWithFlags(&d.ev[s], hipEventDisableTiming);
       if (e != hipSuccess) return fail(WANATTN_E_HIP, "hipEventCreate: %s", hipGetErrorString(e));
@@ -686,6 +702,38 @@ wanattn_status wanattn_self(const void* q, const void* k, const void* v, void* o
   WA_TRY(table_for(theta, (hipStream_t)stream, &tab));
   return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens, workspace, tab, 0,
                      room ? (char*)workspace + bytes : nullptr, room ? items : 0, (hipStream_t)stream);
+}
+
+wanattn_status wanattn_self_noalloc(const void* q, const void* k, const void* v, void* o, int32_t B,
+                                    int32_t N, int32_t heads, int32_t head_dim,
+                                    const wanattn_grid3d* grid, double theta, float scale,
+                                    wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                                    void* stream) {
+  t_err[0] = 0;
+  WA_TRY(check_theta(theta));
+  WA_TRY(check_self_args(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens));
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  const size_t cap = WANATTN_NOALLOC_SCRATCH_BYTES;
+  if (bytes + kQueueBytes > cap)
+    return fail(WANATTN_E_UNSUPPORTED, "B*N*heads = %lld token rows need %zu bytes of scratch; the library holds %zu",
+                (long long)B * N * heads, bytes + kQueueBytes, cap);
+  // (the scratch is an array of its own: it cannot overlap a caller's tensor)
+  unsigned char* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState* d = nullptr;
+    WA_TRY(device_state(&d));
+    ptr = d->scratch;
+  }
+  // the scratch takes the workspace's place: rotated keys, then the split's
+  // partials where they fit, then the queue counters (zeroed by a kernel on
+  // every call); with no room for the partials the queue follows the keys
+  const size_t items = split_items(B, N, heads), full = bytes + items * kSplitItemBytes + kQueueBytes;
+  const size_t room_items = full <= cap ? items : 0;
+  const float2* tab = nullptr;
+  WA_TRY(table_for(theta, (hipStream_t)stream, &tab));
+  return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens, ptr, tab, 0, ptr + bytes,
+                     room_items, (hipStream_t)stream);
 }
 
 size_t wanattn_self_jitter_workspace_bytes(int32_t B, int32_t N, int32_t heads, int32_t head_dim) {

@@ -26,7 +26,9 @@ EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wa
            "wanattn_self_jitter_workspace_bytes", "wanattn_self_kv", "wanattn_rope_tables_bytes",
            "wanattn_rope_tables", "wanattn_rope3d_tables", "wanattn_self_kv_tables",
            "wanattn_cross", "wanattn_prologue", "wanattn_prologue_workspace_bytes", "wanattn_prepare",
-           "wanattn_status_string", "wanattn_last_error", "wanattn_version")
+           "wanattn_status_string", "wanattn_last_error", "wanattn_version", "wanattn_self_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 512 << 20
 
 
 class WanattnError(RuntimeError):
@@ -59,6 +61,8 @@ def load_library(path: str = LIB_PATH):
     lib.wanattn_self.argtypes = [P, P, P, P, i32, i32, i32, i32, G, f64, f32, ctypes.c_int, i32, P,
                                  P, ctypes.c_size_t, P]
     lib.wanattn_self.restype = ctypes.c_int
+    lib.wanattn_self_noalloc.argtypes = [P, P, P, P, i32, i32, i32, i32, G, f64, f32, ctypes.c_int, i32, P, P]
+    lib.wanattn_self_noalloc.restype = ctypes.c_int
     lib.wanattn_self_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.wanattn_self_workspace_bytes.restype = ctypes.c_size_t
     lib.wanattn_self_jitter.argtypes = [P, P, P, P, i32, i32, i32, i32, G, P, f32, ctypes.c_int, i32, P,
@@ -254,6 +258,33 @@ def self_attention(q, k, v, grid, theta: float = 10000.0, scale: float | None = 
     _raise_on(lib.wanattn_self(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, heads, d, ctypes.byref(g),
                                float(theta), float(scale), mask, int(chunk_frames), lens,
                                _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def self_attention_noalloc(q, k, v, grid, theta: float = 10000.0, scale: float | None = None,
+                           block_causal: bool = False, chunk_frames: int = 3, kv_lens=None,
+                           offsets=(0, 0, 0), out=None, stream=None):
+    """self_attention through wanattn_self_noalloc: no workspace, the library's
+    static per-device scratch instead (B * N * heads * 256 + 256 bytes must fit
+    NOALLOC_SCRATCH_BYTES).  Calls that overlap on one device race.  With
+    ``out`` given, nothing is allocated."""
+    import torch
+    lib = load_library()
+    if out is None:
+        with _on(stream):
+            out = torch.empty_like(q)
+    B, N, heads, d = _dims(q, k, v, out)
+    if not (tuple(k.shape) == tuple(v.shape) == tuple(out.shape) == tuple(q.shape)):
+        raise ValueError("q, k, v and out must have the same shape")
+    if kv_lens is not None and len(kv_lens) != B:
+        raise ValueError("kv_lens needs one entry per batch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    g = _grid(grid, offsets)
+    mask = MASK_BLOCK_CAUSAL if block_causal else MASK_NONE
+    _raise_on(lib.wanattn_self_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, heads, d, ctypes.byref(g),
+                                       float(theta), float(scale), mask, int(chunk_frames), _lens(kv_lens, B),
+                                       _stream(stream)))
     return out
 
 

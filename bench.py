@@ -86,6 +86,35 @@ def flops(wl):
     return 4 * d * h * visible_pairs(wl) * wl.batch, 4 * d * h * wl.N * wl.text_len * wl.batch
 
 
+def host_cpus():
+    """The host CPUs this process may use: os.cpu_count(), the affinity set,
+    the cgroup CPU quota (if any) and the CPU model."""
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["affinity"] = os.cpu_count()
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        info["cgroup_quota_cpus"] = None if quota == "max" else round(int(quota) / int(period), 2)
+    except (OSError, ValueError):
+        info["cgroup_quota_cpus"] = None
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    info["model"] = model
+    usable = info["affinity"] or 1
+    if info["cgroup_quota_cpus"]:
+        usable = min(usable, max(1, int(info["cgroup_quota_cpus"] + 0.5)))
+    info["usable"] = usable
+    return info
+
+
 def cpu_baseline(wl, t, threads):
     """Time the fp64 oracle on sampled query rows (all heads) and extrapolate.
 
@@ -139,10 +168,13 @@ def cpu_baseline(wl, t, threads):
     if wl.block_causal:
         b1 *= b / max((t2 - t1) / (len(rows2) - len(rows1)), 1e-12)   # the same visible-key weighting
     t_self1 = a1 + b1 * wl.N
+    cpus = host_cpus()
     return {
         "value": (f_self + f_cross) / (t_self + t_cross) / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "host": {"cpu_model": cpus["model"], "os_cpu_count": cpus["os_cpu_count"], "affinity_cpus": cpus["affinity"],
+                 "cgroup_quota_cpus": cpus["cgroup_quota_cpus"]},
         "kind": "oracle",
         "sample": (f"fp64 oracle on {len(rows1)} and {len(rows2)} sampled query rows x {wl.heads} heads "
                    f"(self, incl. rotating all keys) and {len(rc)} rows (cross); extrapolated as "
@@ -311,6 +343,49 @@ def prologue_leg(torch, seeded, wa, wl, steps, warmup):
             "floor_ms": round(floor_ms, 3), "frac_of_floor": round(floor_ms / ms, 4)}
 
 
+METRIC_WORKLOADS = ("wan14b_480p_81f", "wan13b_480p_81f", "wan14b_720p_81f")
+
+
+def metric_points(torch, seeded, wa, wl_main, main_tflops, main_ms, steps, warmup):
+    """Self attention (wanattn_self, the benchmark's launch configuration) at
+    every size the metric names: 32,760 tokens (40 and 12 heads) and 75,600
+    tokens (40 heads, the step's own figures).  HIP events on the launch stream."""
+    import numpy as np
+    points = []
+    for name in METRIC_WORKLOADS:
+        wl = seeded.WORKLOADS[name]
+        f_self, _ = flops(wl)
+        if name == wl_main.name:
+            ms, tf = main_ms, main_tflops
+        else:
+            t = seeded.workload_tensors(wl, seed=0, cross=False)
+            dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+            q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+            o = torch.empty_like(q)
+            ws = torch.empty(wa.self_workspace_bytes(wl.batch, wl.N, wl.heads), dtype=torch.uint8, device="cuda")
+            grid = (wl.F, wl.H, wl.W)
+            stream = torch.cuda.current_stream()
+            call = lambda: wa.self_attention(q, k, v, grid, block_causal=wl.block_causal,
+                                             chunk_frames=wl.chunk_frames, out=o, workspace=ws)
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                call()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+            tf = f_self / (ms * 1e-3) / 1e12
+            del q, k, v, o, ws
+            torch.cuda.empty_cache()
+        log(f"metric point {name}: {wl.N} tokens x {wl.heads} heads: self {ms:.3f} ms, {tf:.1f} TFLOP/s")
+        points.append({"workload": name, "tokens": wl.N, "heads": wl.heads, "self_ms": round(ms, 3),
+                       "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+    return points
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +394,8 @@ def main():
     ap.add_argument("--workload", default="wan14b_720p_81f")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-metric-points", action="store_true",
+                    help="skip timing self attention at the metric's other sizes (32,760 tokens x 40 and 12 heads)")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--kv-stream", action="store_true",
                     help="also time one Self Forcing streaming step: the last 3-frame chunk of the "
@@ -458,8 +535,11 @@ def main():
         result["jitter"] = jitter_leg(torch, seeded, wa, wl, q, k, v, args.steps, args.warmup)
     if args.prologue:
         result["prologue"] = prologue_leg(torch, seeded, wa, wl, args.steps, args.warmup)
+    if not args.no_metric_points:
+        result["metric_points"] = metric_points(torch, seeded, wa, wl, achieved, self_avg, args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
+        # every CPU this process may run on (the affinity set, within any cgroup quota)
+        threads = args.cpu_threads or host_cpus()["usable"]
         result["cpu_baseline"] = cpu_baseline(wl, t, threads)
     print(json.dumps(result), flush=True)
 

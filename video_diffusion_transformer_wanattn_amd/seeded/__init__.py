@@ -28,6 +28,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libseeded.so")
+# tests/test_sanitizers.py points this at a build with the address and
+# undefined-behaviour sanitizers
+_OVERRIDE = os.environ.get("WANATTN_SEEDED_LIB")
 
 # Tensor ids inside a workload; stream = workload_id * 16 + tensor id.
 Q, K, V, TEXT_K, TEXT_V = 0, 1, 2, 3, 4
@@ -72,9 +75,10 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
-        lib = ctypes.CDLL(LIB_PATH)
+        path = _OVERRIDE or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+        lib = ctypes.CDLL(path)
         lib.seeded_normal_bf16.restype = ctypes.c_int
         lib.seeded_normal_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                            ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double,

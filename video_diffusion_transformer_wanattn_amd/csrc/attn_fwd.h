@@ -69,6 +69,16 @@ constexpr int kVHalves = 4 * kHalfTile;        // V halves of the 4 stages start
 constexpr int kStages = 4;
 constexpr int kLdsBytes = kStages * kTileBytes;  // 128 KiB of 160
 constexpr float kLazySum = 65536.0f;           // lane partial block sum that moves the reference
+// Cross attention's persistent launch prefetches the next item during the
+// epilogue: its first two tiles into stages 0 and 1, its 256 query rows into
+// the K' and V halves of stages 2 and 3 (wave w's 64 rows at kPrefetchQ[w];
+// tile 2 overwrites them only after the next item's first barrier), and the
+// output is staged in 32-row halves above the stages.
+constexpr int kPrefetchStaging = 128 * 1024;                                    // 8 KiB per wave
+constexpr int kLdsPrefetchBytes = kPrefetchStaging + kWaves * 32 * kRowBytes;  // 160 KiB
+__device__ __forceinline__ int prefetch_q_base(int wave) {
+  return wave < 2 ? 2 * kHalfTile + wave * 64 * kRowBytes : kVHalves + 2 * kHalfTile + (wave - 2) * 64 * kRowBytes;
+}
 
 struct AttnParams {
   const uint16_t* q;
@@ -184,10 +194,17 @@ __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t
 
 template <bool ROPE, bool CAUSAL, bool PERSIST = false>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg) {
+  // Cross attention's persistent launch (PERSIST without RoPE) takes its items
+  // in a fixed order, with no queue, and issues the next item's first two
+  // key tiles and its query loads before the current item's epilogue, whose
+  // output staging then moves above the stages (kPrefetchStaging).  Its items
+  // are short (512 text keys), so the per-item query load and epilogue would
+  // otherwise take about half of each one.
+  constexpr bool PREFETCH = PERSIST && !ROPE;
   // LDS: the K' halves of the 4 stages in the first 64 KiB, their V halves in
   // the second, so that every operand read is one base register (per lane)
   // plus an immediate offset below 64 KiB (the ds_read offset field)
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[PREFETCH ? kLdsPrefetchBytes : kLdsBytes];
   // K' half of a stage, as a compile-time constant (main loop) or a run-time
   // index (masked tail); its V half is kVHalves further
   auto stage = [&](auto S) __attribute__((always_inline)) -> char* {
@@ -202,6 +219,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
   __shared__ int s_item;
   int cursor = 0;  // lane 0 of wave 0: the queue it draws from (next_item)
   const int xcc = PERSIST ? (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7) : 0;  // HW_REG_XCC_ID
+  // fixed item order of the prefetching launch: workgroup w (of 8 c, run on XCD
+  // w % 8) takes items w / 8, w / 8 + c, ... of XCD w % 8's contiguous run
+  int pass = 0;
+  bool pre = false;   // this pass's first two tiles and its queries were loaded last pass
+  auto static_item = [&](const auto& pp, int ps) -> int {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3, c = gridDim.x >> 3;
+    const int per = pp.total >> 3, rem = pp.total & 7;
+    const int idx = j + c * ps;
+    return idx < per + (x < rem ? 1 : 0) ? x * per + (x < rem ? x : rem) + idx : -1;
+  };
 
   // one work item per pass; a plain launch makes one pass
   for (;;) {
@@ -230,7 +257,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     // A split item takes key range ks of tile total + item / nsplit.
     int L, ks = 0, item = 0;
     bool split = false;
-    if constexpr (PERSIST) {
+    if constexpr (PREFETCH) {
+      L = static_item(p, pass);
+      if (L < 0) break;
+    } else if constexpr (PERSIST) {
       // every thread has read the previous item (its pass had barriers since)
       if (tid == 0) s_item = next_item(p_arg, xcc, cursor);
       __syncthreads();
@@ -335,16 +365,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     // stage: with fewer tiles than stages that stage was never filled, so zero
     // the stages then (with more, it holds an earlier tile: finite values whose
     // scores are discarded).  nt is uniform over the workgroup.
-    if (nt < kStages) {
+    if (!(PREFETCH && pre)) {
+      if (nt < kStages) {
   #pragma unroll
-      for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i)
-        *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
-      tile_barrier();
-    }
+        for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i)
+          *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
+        tile_barrier();
+      }
 
-    // prefetch the first two tiles while the queries are loaded
-    issue_tile(S0{}, 0);
-    if (nt > 1) issue_tile(S1{}, 1);
+      // prefetch the first two tiles while the queries are loaded
+      issue_tile(S0{}, 0);
+      if (nt > 1) issue_tile(S1{}, 1);
+    }
 
     // ---- Q: load, rotate, scale, round to bf16; kept in registers as the B
     // operand of K Q^T: lane holds d = 16 kk + 8 hh + 0..7 of its query.
@@ -369,8 +401,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         pw[qb] = w + p.w0;
       }
       const u32x4* src = (const u32x4*)(qbase + (size_t)ic * row_stride);
+      if (PREFETCH && pre) {
+        // from LDS, where this wave's own loads put its rows last pass (row
+        // rho's chunk c stored at c ^ (rho & 15)); only the output stores of
+        // the last epilogue may still be outstanding
+        if (qb == 0) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        const int rho = qb * 32 + r;
+        const char* qrow = lds + prefetch_q_base(wave) + rho * kRowBytes;
   #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qraw[qb][kk] = src[2 * kk + hh];
+        for (int kk = 0; kk < 8; ++kk) qraw[qb][kk] = *(const u32x4*)(qrow + 16 * ((2 * kk + hh) ^ (rho & 15)));
+      } else {
+  #pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qraw[qb][kk] = src[2 * kk + hh];
+      }
     }
   #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -569,9 +612,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     };
 
     // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored and
-    // finished, K' operands of block 1 loaded
-    if (nt > 1) wait_vm<8>();
-    else wait_vm<0>();
+    // finished, K' operands of block 1 loaded (prefetched tiles are resident
+    // since the wait for the prefetched queries, which were loaded after them)
+    if (!(PREFETCH && pre)) {
+      if (nt > 1) wait_vm<8>();
+      else wait_vm<0>();
+    }
     tile_barrier();
     if (nt > 2) issue_tile(S2{}, 2);
     load_kops(S0{}, 0);
@@ -684,7 +730,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[0][db]) : "a"(vop[db][sl]), "v"(pb[0][sl]));
         if (g == 0) {
           take_scores();
-          if constexpr (decltype(MASKED)::value) mask_scores(j + 1);
+          // (tail tiles: only blocks that reach past a row's visible keys)
+          if constexpr (decltype(MASKED)::value)
+            if (32 * (j + 1) + 32 > kv_full) mask_scores(j + 1);
         }
         // the exps after this product, not hoisted above it (the two products
         // of a group would otherwise issue back to back)
@@ -774,6 +822,80 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     acc_fence();
     wait_vm<0>();
     tile_barrier();
+    if constexpr (PREFETCH) {
+      // the next item's first two tiles (into stages 0 and 1, which every
+      // wave has left) and its query loads, issued before this epilogue
+      pre = false;
+      const int Ln = static_item(p, pass + 1);
+      if (Ln >= 0) {
+        const int bhn = Ln / p.ntq, tqn = Ln - bhn * p.ntq;
+        const int bn = bhn / p.heads, headn = bhn - bn * p.heads;
+        // (an item with fewer tiles than stages zeroes the stages first)
+        if ((p.lens[bn] + kBN - 1) / kBN >= kStages) {
+          const char* kn = (const char*)(p.k + ((size_t)bn * p.Nk * p.heads + headn) * kHeadDim);
+          const char* vn = (const char*)(p.v + ((size_t)bn * p.Nk * p.heads + headn) * kHeadDim);
+          const uint32_t st0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S0{});
+          const uint32_t st1 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage(S1{});
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int blk = 4 * wave + i;
+            dma16(kn, koff_ld[i], st0 + blk * 1024);
+            dma16(vn, voff_ld[i], st0 + kVHalves + blk * 1024);
+          }
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int blk = 4 * wave + i;
+            dma16(kn + (size_t)kBN * rsb, koff_ld[i], st1 + blk * 1024);
+            dma16(vn + (size_t)kBN * rsb, voff_ld[i], st1 + kVHalves + blk * 1024);
+          }
+          // this wave's 64 query rows: instruction i fills rows 4 i + lane / 16,
+          // stored chunk lane % 16 holding chunk (lane % 16) ^ (row & 15)
+          // (rows past the last token repeat it; a wave whose rows all lie past
+          // it, in a partial last tile, reads the last token's row: the load
+          // base is the wave's first row clamped, so every offset is 0..63 rows)
+          const int ibase = tqn * kBM + wave * 64;
+          const int ib0 = min(ibase, p.N - 1);
+          const char* qn = (const char*)(p.q + (((size_t)bn * p.N + ib0) * p.heads + headn) * kHeadDim);
+          const uint32_t qst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds + prefetch_q_base(wave));
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = 4 * i + ld_row;
+            const int rowc = min(ibase + row, p.N - 1) - ib0;
+            dma16(qn, (uint32_t)rowc * rsb + 16 * (ld_chunk ^ (row & 15)), qst + i * 1024);
+          }
+          pre = true;
+        }
+      }
+      ++pass;
+    }
+    if constexpr (PREFETCH) {
+      // O in two 32-row halves through this wave's 8 KiB above the stages
+      char* orows = lds + kPrefetchStaging + wave * (32 * kRowBytes);
+      const int sr = lane >> 4, sc = lane & 15;
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float inv = 1.0f / wave_half_sum(lrun[qb]);
+  #pragma unroll
+        for (int db = 0; db < 4; ++db)
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv);
+            w[1] = pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv);
+            *(u32x2*)(orows + r * kRowBytes + 16 * ((4 * db + g4) ^ (r & 15)) + 8 * hh) = w;
+          }
+        const int irow0 = i0 + wave * 64 + qb * 32 + sr;
+        uint16_t* dst = p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc;
+  #pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int row = 4 * it + sr;
+          const u32x4 w = *(const u32x4*)(orows + row * kRowBytes + 16 * (sc ^ (row & 15)));
+          if (irow0 + 4 * it < p.N) *(u32x4*)dst = w;
+          dst += 4 * row_stride;
+        }
+      }
+      continue;
+    }
     char* orows = lds + wave * (64 * kRowBytes);
   #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {

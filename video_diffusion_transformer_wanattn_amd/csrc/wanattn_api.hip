@@ -332,6 +332,18 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
         continue;
       }
     }
+    if constexpr (!ROPE && !CAUSAL) {
+      // cross attention: one workgroup per compute unit (a multiple of 8, so
+      // that each XCD gets the same share), items in a fixed order, each
+      // workgroup issuing its next item's first loads before its epilogue
+      const int ncu = device_cus();
+      const int grid = (ncu / 8) * 8;
+      if (grid >= 8 && p.total >= grid) {
+        hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        WA_TRY(launched("cross attention"));
+        continue;
+      }
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<ROPE, CAUSAL>), dim3(p.total), dim3(kThreads), 0, stream, p);
     WA_TRY(launched("attention"));
   }

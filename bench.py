@@ -337,10 +337,46 @@ def prologue_leg(torch, seeded, wa, wl, steps, warmup):
     row_bytes = 2 * rows * dim * 2 + 4 * rows * dim * 2     # LayerNorm x -> y, RMSNorm q, k in place
     floor_ms = gemm_flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3 + row_bytes / (PEAK_HBM_GBS * 1e9) * 1e3
     log(f"prologue: {rows} tokens x dim {dim}: {ms:.3f} ms (floor {floor_ms:.3f} ms)")
-    return {"workload": f"{wl.name} prologue: {rows} tokens x dim {dim}", "ms": round(ms, 3),
-            "gemm_flops": gemm_flops, "row_pass_bytes": row_bytes,
-            "tflops_over_gemm_flops": round(gemm_flops / (ms * 1e-3) / 1e12, 2),
-            "floor_ms": round(floor_ms, 3), "frac_of_floor": round(floor_ms / ms, 4)}
+    res = {"workload": f"{wl.name} prologue: {rows} tokens x dim {dim}", "ms": round(ms, 3),
+           "gemm_flops": gemm_flops, "row_pass_bytes": row_bytes,
+           "tflops_over_gemm_flops": round(gemm_flops / (ms * 1e-3) / 1e12, 2),
+           "floor_ms": round(floor_ms, 3), "frac_of_floor": round(floor_ms / ms, 4)}
+
+    # the block up to the attention output, two ways: the prologue with the
+    # RMSNorm in place then wanattn_self, or the prologue that leaves the
+    # RMSNorm to wanattn_self_qknorm (one pass over q and k fewer)
+    shp = (wl.batch, wl.N, wl.heads, wl.head_dim)
+    grid = (wl.F, wl.H, wl.W)
+    o = torch.empty(shp, dtype=torch.bfloat16, device="cuda")
+    rms = torch.empty(2, rows, dtype=torch.float32, device="cuda")
+    sws = torch.empty(wa.self_workspace_bytes(*shp), dtype=torch.uint8, device="cuda")
+    kw = dict(block_causal=wl.block_causal, chunk_frames=wl.chunk_frames, out=o, workspace=sws)
+    qv, kv, vv = (t.view(shp) for t in out)
+
+    def block_in_place():
+        wa.prologue(d["x"], e0, e1, d["wq"], d["bq"], d["wk"], d["bk"], d["wv"], d["bv"], d["gq"], d["gk"],
+                    out=out, workspace=ws)
+        wa.self_attention(qv, kv, vv, grid, **kw)
+
+    def block_deferred():
+        wa.prologue_rms(d["x"], e0, e1, d["wq"], d["bq"], d["wk"], d["bk"], d["wv"], d["bv"], out=out, rms=rms,
+                        workspace=ws)
+        wa.self_attention_qknorm(qv, kv, vv, rms, d["gq"], d["gk"], grid, **kw)
+
+    bsteps = max(2, min(steps, 5))
+    for name, fn in (("block_norm_in_place_ms", block_in_place), ("block_norm_deferred_ms", block_deferred)):
+        for _ in range(max(1, min(warmup, 2))):
+            fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(bsteps)]
+        for e in evs:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(sum(e[0].elapsed_time(e[1]) for e in evs) / bsteps, 3)
+        log(f"block ({name}): {res[name]:.3f} ms")
+    return res
 
 
 METRIC_WORKLOADS = ("wan14b_480p_81f", "wan13b_480p_81f", "wan14b_720p_81f")

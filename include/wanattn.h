@@ -294,6 +294,42 @@ wanattn_status wanattn_prologue(const void* x, const float* e0, const float* e1,
 size_t wanattn_prologue_workspace_bytes(int32_t B, int32_t N, int32_t dim);
 
 /*
+ * [P1] ch. 4, the same prologue with the QK-Norm left to the attention call
+ * that reads q and k ("3D RoPE": q and k are RMS-normalised, then rotated):
+ * q and k are written as projected (before the RMSNorm), v as in
+ * wanattn_prologue, and
+ *   rms[t] = 1 / sqrt(mean(q[t]^2) + eps_rms),  rms[B*N + t] = the same for k
+ * for every token row t (fp32, caller-owned device memory of 2*B*N floats,
+ * 16-byte aligned, not overlapping any tensor or the workspace).
+ * wanattn_self_qknorm then applies q * rms * gq and k * rms * gk where it
+ * loads the queries and where it rotates the keys, so that q and k are not
+ * written twice.  Arguments otherwise as wanattn_prologue (gq, gk are given
+ * to wanattn_self_qknorm instead); the workspace is
+ * wanattn_prologue_workspace_bytes(B, N, dim).
+ */
+wanattn_status wanattn_prologue_rms(const void* x, const float* e0, const float* e1, const void* wq,
+                                    const void* bq, const void* wk, const void* bk, const void* wv,
+                                    const void* bv, void* q, void* k, void* v, float* rms, int32_t B,
+                                    int32_t N, int32_t dim, float eps_ln, float eps_rms, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
+ * wanattn_self on the outputs of wanattn_prologue_rms: q and k are the
+ * projections before the QK-Norm ([B, N, heads, 128] bf16), rms its factors
+ * (q's B*N, then k's B*N, fp32, 4-byte aligned), gq and gk its weights
+ * ([heads * 128] bf16, 16-byte aligned).  Each query element is taken as
+ * q * rms * gq as it is loaded, each key element as k * rms * gk as the key
+ * is rotated into the workspace, in fp32, before the rotation; the rest,
+ * including the workspace (wanattn_self_workspace_bytes), errors and
+ * numerics, is as wanattn_self.
+ */
+wanattn_status wanattn_self_qknorm(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t N,
+                                   int32_t heads, int32_t head_dim, const wanattn_grid3d* grid, double theta,
+                                   float scale, wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                                   const float* rms, const void* gq, const void* gk, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * Build the rotary table for theta on the current device now and wait for it
  * (a blocking call on the null stream).  Optional: the first call that uses
  * theta builds it otherwise.  Up to 8 distinct theta values are kept per

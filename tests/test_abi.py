@@ -315,6 +315,56 @@ def test_prologue_rejects(lib):
     assert lib.wanattn_last_error()
 
 
+def test_prologue_rms_rejects(lib):
+    # the prologue that leaves the QK-Norm to the attention call: 13 tensors
+    # (no gammas) and the factors' buffer, checked like the prologue's
+    base = [ctypes.c_void_p((i + 1) << 32) for i in range(12)]
+    rms = ctypes.c_void_p(13 << 32)
+    ws = ctypes.c_void_p(15 << 32)
+
+    def call(ptrs=None, rms=rms, B=1, N=24, dim=256, ws=ws, ws_bytes=24 * 256 * 2 + GEMM_WS):
+        ptrs = list(base) if ptrs is None else ptrs
+        return lib.wanattn_prologue_rms(*ptrs, rms, B, N, dim, 1e-6, 1e-6, ws, ws_bytes, None)
+
+    assert call(rms=None) == wa.E_INVALID
+    assert "rms" in lib.wanattn_last_error().decode()
+    assert call(rms=ctypes.c_void_p((13 << 32) + 4)) == wa.E_INVALID             # not 16-byte aligned
+    for i in range(12):
+        ptrs = list(base)
+        ptrs[i] = None
+        assert call(ptrs) == wa.E_INVALID, i
+    assert call(rms=ctypes.c_void_p((12 << 32) + 256)) == wa.E_INVALID           # rms inside v
+    assert "rms overlaps" in lib.wanattn_last_error().decode()
+    assert call(rms=ctypes.c_void_p((15 << 32) + 4096)) == wa.E_INVALID          # rms inside the workspace
+    assert call(dim=12) == wa.E_INVALID
+    assert call(ws_bytes=24 * 256 * 2 + GEMM_WS - 1) == wa.E_INVALID
+
+
+def test_self_qknorm_rejects(lib):
+    # self attention with the QK-Norm applied in the call: the self checks,
+    # then the factors and the gammas
+    R = ctypes.c_void_p(6 << 30)
+    GQ = ctypes.c_void_p(7 << 30)
+    GK = ctypes.c_void_p(8 << 30)
+
+    def call(rms=R, gq=GQ, gk=GK, o=O, N=24, ws=WS, ws_bytes=1 << 20, theta=1e4):
+        return lib.wanattn_self_qknorm(A, B_, C, o, 1, N, 2, 128, g(2, 3, 4), theta, 0.088, 0, 3, None,
+                                       rms, gq, gk, ws, ws_bytes, None)
+
+    for kw in (dict(rms=None), dict(gq=None), dict(gk=None)):
+        assert call(**kw) == wa.E_INVALID, kw
+        assert "gq" in lib.wanattn_last_error().decode()
+    assert call(rms=ctypes.c_void_p((6 << 30) + 2)) == wa.E_INVALID               # rms not 4-byte aligned
+    assert call(gq=ctypes.c_void_p((7 << 30) + 8)) == wa.E_INVALID                # gamma not 16-byte aligned
+    assert call(rms=ctypes.c_void_p((4 << 30) + 64)) == wa.E_INVALID              # rms inside o
+    assert "o overlaps" in lib.wanattn_last_error().decode()
+    assert call(gk=ctypes.c_void_p((5 << 30) + 64)) == wa.E_INVALID               # gamma inside the workspace
+    assert "workspace overlaps" in lib.wanattn_last_error().decode()
+    assert call(N=25) == wa.E_INVALID                                             # N != F*H*W
+    assert call(theta=0.0) == wa.E_INVALID
+    assert call(ws_bytes=16) == wa.E_INVALID                                      # workspace too small
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(1, 24, 2, 128, dtype=torch.bfloat16)

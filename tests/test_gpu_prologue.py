@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from parity_util import errors, from_dev, to_dev, widen
+from parity_util import assert_parity, errors, from_dev, to_dev, widen
 from video_diffusion_transformer_wanattn_amd import seeded
 from video_diffusion_transformer_wanattn_amd import wanattn as wa
 
@@ -127,3 +127,89 @@ def test_prologue_errors():
     e12 = torch.zeros(1, 12, device="cuda")
     with pytest.raises(wa.WanattnError):
         wa.prologue(x12, e12, e12, w12, b12, w12, b12, w12, b12, b12, b12)
+
+
+# ---------------------------------------------------------------------------
+# the QK-Norm deferred to the attention call (wanattn_prologue_rms +
+# wanattn_self_qknorm): the RMSNorm factors as the in-place path computes
+# them, and a whole block against the oracle's prologue then attention
+# ---------------------------------------------------------------------------
+
+def gpu_prologue_rms(d, eps_ln=1e-6, eps_rms=1e-6):
+    out = wa.prologue_rms(d["x"], d["e0"], d["e1"], d["wq"], d["bq"], d["wk"], d["bk"], d["wv"], d["bv"],
+                          eps_ln=eps_ln, eps_rms=eps_rms)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("B,N,dim,shift", [(2, 37, 256, 0.0), (2, 65, 640, 20.0)])
+def test_prologue_rms_factors_match_the_in_place_norm(B, N, dim, shift):
+    t = seeded.prologue_tensors(B, N, dim, seed=80 + dim, x_shift=shift, x_sigma=4.0 if shift else 1.0)
+    d = to_dev_inputs(t)
+    q, k, v = gpu_prologue(d)
+    qr, kr, vr, rms = gpu_prologue_rms(d)
+    np.testing.assert_array_equal(from_dev(vr), from_dev(v))
+    # the in-place path rounds (x * factor) * gamma in fp32 to bf16: the
+    # deferred outputs with the same factors give the same bits
+    r = rms.cpu().numpy().reshape(2, B * N, 1).astype(np.float32)
+    for i, (raw, normed, g) in enumerate(((qr, q, t["gq"]), (kr, k, t["gk"]))):
+        x = seeded.bf16_bits_to_f32(from_dev(raw)).reshape(B * N, dim)
+        y = (x * r[i]) * seeded.bf16_bits_to_f32(g)[None, :]
+        np.testing.assert_array_equal(seeded.f32_to_bf16_bits_array(y), from_dev(normed).reshape(B * N, dim))
+    rq, rk, rv = oracle_prologue(t)
+    gam = seeded.bf16_bits_to_f32(t["gq"]).astype(np.float64)
+    xq = seeded.bf16_bits_to_f32(from_dev(qr)).astype(np.float64).reshape(B, N, dim)
+    approx = xq * r[0].reshape(B, N, 1) * gam
+    e = errors(seeded.f32_to_bf16_bits_array(approx.astype(np.float32)), rq)
+    assert e["rel_rms"] <= REL_RMS, e
+
+
+def block_inputs(F, H, W, heads, seed):
+    N, dim = F * H * W, heads * 128
+    t = seeded.prologue_tensors(1, N, dim, seed=seed)
+    return t, to_dev_inputs(t), N, dim
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_with_deferred_qk_norm_matches_oracle(causal):
+    # prologue then self attention, QK-Norm applied in the attention call,
+    # against the oracle's prologue (fp64) whose q, k, v (as bf16, the
+    # attention's inputs) go through the oracle's attention; every row
+    F, H, W, heads = 4, 8, 12, 4
+    t, d, N, dim = block_inputs(F, H, W, heads, 90 + causal)
+    shp = (1, N, heads, 128)
+    kw = dict(block_causal=True, chunk_frames=2, kv_lens=[300]) if causal else {}
+    qr, kr, vr, rms = gpu_prologue_rms(d)
+    o = wa.self_attention_qknorm(qr.view(shp), kr.view(shp), vr.view(shp), rms, d["gq"], d["gk"], (F, H, W), **kw)
+    q, k, v = gpu_prologue(d)
+    o_ref_gpu = wa.self_attention(q.view(shp), k.view(shp), v.view(shp), (F, H, W), **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle_prologue(t)
+    bits = [seeded.f32_to_bf16_bits_array(a.astype(np.float32)).reshape(shp) for a in (rq, rk, rv)]
+    ref = oracle.self_rows(*bits, (F, H, W), theta=10000.0, **kw)
+    got = from_dev(o)
+    e = assert_parity(got, ref, what=f"block, deferred QK-Norm, causal={causal}")
+    e2 = errors(got, widen(from_dev(o_ref_gpu)))
+    print(f"block deferred QK-Norm causal={causal}: vs oracle {e}; vs in-place path {e2}", flush=True)
+    assert e2["rel_rms"] <= REL_RMS
+
+
+def test_block_with_deferred_qk_norm_at_full_size():
+    # the Wan 14B block at 720p: 75,600 tokens x dim 5120 (40 heads), the
+    # deferred path against the in-place one on the GPU (the oracle's whole
+    # prologue at this size is out of reach), every row
+    F, H, W, heads = 21, 45, 80, 40
+    t, d, N, dim = block_inputs(F, H, W, heads, 92)
+    shp = (1, N, heads, 128)
+    qr, kr, vr, rms = gpu_prologue_rms(d)
+    o = wa.self_attention_qknorm(qr.view(shp), kr.view(shp), vr.view(shp), rms, d["gq"], d["gk"], (F, H, W))
+    del qr, kr, vr
+    q, k, v = gpu_prologue(d)
+    o_ref = wa.self_attention(q.view(shp), k.view(shp), v.view(shp), (F, H, W))
+    torch.cuda.synchronize()
+    diff = (o.float() - o_ref.float())
+    rel = float(torch.sqrt(torch.mean(diff * diff)) / torch.sqrt(torch.mean(o_ref.float() ** 2)))
+    mx = float(diff.abs().max())
+    print(f"block at 75,600 x 5120, deferred vs in-place QK-Norm: rel_rms {rel:.3e} max {mx:.3e}", flush=True)
+    assert bool(torch.isfinite(o.float()).all())
+    assert rel <= REL_RMS and mx <= 2e-2

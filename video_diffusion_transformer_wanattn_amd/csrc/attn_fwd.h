@@ -107,6 +107,10 @@ struct AttnParams {
   float4* part_o;
   float2* part_lb;
   int nsplit, nsplit_items;
+  // QK-Norm of the queries applied as they are loaded (QNORM kernels): q *
+  // q_rms[b * N + n] * gq[head * 128 + d] before the rotation
+  const float* q_rms;
+  const uint16_t* gq;
   int lens[WANATTN_MAX_LEN_BATCH];  // visible keys per batch (1..Nk)
 };
 
@@ -137,10 +141,12 @@ __device__ __forceinline__ int row_limit(const P& p, int kvl, int i) {
   return lim;
 }
 
+// (sre, sim: factors applied before the rotation, 1 unless the queries are
+// RMS-normalised here)
 template <bool ROPE>
 __device__ __forceinline__ uint32_t rotate_pair(uint32_t w, const float2* tab, int c, int pf, int ph,
-                                                int pw, float scale) {
-  float re = bf16_lo(w), im = bf16_hi(w);
+                                                int pw, float scale, float sre = 1.0f, float sim = 1.0f) {
+  float re = bf16_lo(w) * sre, im = bf16_hi(w) * sim;
   if (ROPE) {
     int a = pair_axis(c);
     int pa = a == 0 ? pf : (a == 1 ? ph : pw);
@@ -192,7 +198,7 @@ __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
 }
 
-template <bool ROPE, bool CAUSAL, bool PERSIST = false>
+template <bool ROPE, bool CAUSAL, bool PERSIST = false, bool QNORM = false>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg) {
   // Cross attention's persistent launch (PERSIST without RoPE) takes its items
   // in a fixed order, with no queue, and issues the next item's first two
@@ -415,16 +421,40 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         for (int kk = 0; kk < 8; ++kk) qraw[qb][kk] = src[2 * kk + hh];
       }
     }
+    if constexpr (QNORM) {
+      // RMSNorm of the queries: each row's factor times the head's gamma (d = 16
+      // kk + 8 hh + 0..7 in chunk kk), then the rotation
+      float qs[2];
   #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb) {
+        const int i = i0 + wave * 64 + qb * 32 + r;
+        qs[qb] = p.q_rms[(size_t)b * p.N + (i < p.N ? i : p.N - 1)];
+      }
   #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        u32x4 pk;
+        const u32x4 gw = *(const u32x4*)(p.gq + (size_t)head * kHeadDim + 16 * kk + 8 * hh);
   #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pk[e] = rotate_pair<ROPE>(qraw[qb][kk][e], qtab, 8 * kk + 4 * hh + e, pf[qb], ph[qb], pw[qb], p.qscale);
-        qf[qb][kk] = __builtin_bit_cast(bf16x8, pk);
+        for (int qb = 0; qb < 2; ++qb) {
+          u32x4 pk;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pk[e] = rotate_pair<ROPE>(qraw[qb][kk][e], qtab, 8 * kk + 4 * hh + e, pf[qb], ph[qb], pw[qb], p.qscale,
+                                      qs[qb] * bf16_lo(gw[e]), qs[qb] * bf16_hi(gw[e]));
+          qf[qb][kk] = __builtin_bit_cast(bf16x8, pk);
+        }
       }
+    } else {
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+  #pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          u32x4 pk;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pk[e] = rotate_pair<ROPE>(qraw[qb][kk][e], qtab, 8 * kk + 4 * hh + e, pf[qb], ph[qb], pw[qb], p.qscale);
+          qf[qb][kk] = __builtin_bit_cast(bf16x8, pk);
+        }
+    }
     // keep Q in AGPRs: the MFMA reads its B operand from there directly and the
     // arch VGPRs stay free for the scores and the softmax
     asm volatile(""

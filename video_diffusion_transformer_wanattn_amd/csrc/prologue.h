@@ -130,6 +130,41 @@ __global__ void __launch_bounds__(256) qk_rmsnorm_kernel(RmsParams p) {
   }
 }
 
+struct RmsStatParams {
+  const uint16_t* q;    // [rows, dim] bf16 (q, k projections before the RMSNorm)
+  const uint16_t* k;
+  float* rms;           // [2][rows]: 1 / sqrt(mean(x^2) + eps) of each q row, then each k row
+  long long rows;
+  int dim;
+  float eps;
+};
+
+// The RMSNorm's factor of every q and k row, the rows left as they are: the
+// attention call applies x * factor * gamma where it reads q and rotates k.
+// One wave per row; reads each row once and writes one float.
+template <int NCH>
+__global__ void __launch_bounds__(256) qk_rms_stats_kernel(RmsStatParams p) {
+  const int lane = threadIdx.x & 63;
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= 2 * p.rows) return;
+  const bool is_k = r >= p.rows;
+  const uint16_t* xr = (is_k ? p.k : p.q) + (is_k ? r - p.rows : r) * p.dim;
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = i * 512 + lane * 8;
+    if (c >= p.dim) continue;
+    const u32x4 w = *(const u32x4*)(xr + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf16_lo(w[e]), d = bf16_hi(w[e]);
+      ss += a * a + d * d;
+    }
+  }
+  const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)p.dim + p.eps);
+  if (lane == 0) p.rms[r] = inv;
+}
+
 // launch either kernel with NCH = ceil(dim / 512) (1 <= NCH <= kMaxRowChunks)
 template <template <int> class Launch, typename P>
 hipError_t launch_rows(int dim, dim3 grid, hipStream_t st, const P& p) {
@@ -149,6 +184,14 @@ template <int NCH>
 struct LnModLaunch {
   static hipError_t run(dim3 grid, hipStream_t st, const LnModParams& p) {
     hipLaunchKernelGGL(ln_mod_kernel<NCH>, grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
+};
+
+template <int NCH>
+struct QkRmsStatLaunch {
+  static hipError_t run(dim3 grid, hipStream_t st, const RmsStatParams& p) {
+    hipLaunchKernelGGL(qk_rms_stats_kernel<NCH>, grid, dim3(256), 0, st, p);
     return hipGetLastError();
   }
 };

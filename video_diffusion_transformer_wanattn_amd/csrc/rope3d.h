@@ -19,6 +19,10 @@ struct RopeParams {
   u32x4* y;
   const float2* tab;
   long long tab_hstride;  // float2 entries between consecutive heads' tables (0: one shared table)
+  // optional QK-Norm applied before the rotation (null: none): x * rms[token
+  // row] * gamma[head * 128 + d], rms indexed by b * N + n
+  const float* rms;
+  const uint16_t* gamma;
   long long chunks;  // B * N * heads * 16
   int N, heads, H, W;
   int f0, h0, w0;
@@ -38,13 +42,19 @@ __global__ void __launch_bounds__(256) rope3d_kernel(RopeParams p) {
     divmod(rem, p.W, p.inv_w, h, w);
     u32x4 in = p.x[idx];
     u32x4 out;
+    float s = 1.0f;
+    u32x4 g = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 ones
+    if (p.rms) {
+      s = p.rms[tok];
+      g = *(const u32x4*)(p.gamma + (tok_head - tok * p.heads) * kHeadDim + 8 * dc);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       int c = 4 * dc + e;
       int a = pair_axis(c);
       int pa = a == 0 ? f + p.f0 : (a == 1 ? h + p.h0 : w + p.w0);
       float2 cs = tab[(a * kMaxPos + pa) * kTabStride + pair_index(c)];
-      float re = bf16_lo(in[e]), im = bf16_hi(in[e]);
+      float re = bf16_lo(in[e]) * s * bf16_lo(g[e]), im = bf16_hi(in[e]) * s * bf16_hi(g[e]);
       out[e] = pack_bf16x2(re * cs.x - im * cs.y, re * cs.y + im * cs.x);
     }
     p.y[idx] = out;

@@ -292,12 +292,13 @@ int choose_split(int total, int ncu, int minlen, size_t room, int* tail_out) {
 // per-batch key lengths always fit the kernel argument block.  `part` (room
 // for part_items split items followed by kQueueBytes, or null) enables
 // persistent launches and tail splitting.
-template <bool ROPE, bool CAUSAL>
+template <bool ROPE, bool CAUSAL, bool QNORM = false>
 wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStream_t stream,
                            void* part = nullptr, size_t part_items = 0) {
   const size_t qstride = (size_t)p.N * p.heads * kHeadDim, kstride = (size_t)p.Nk * p.heads * kHeadDim;
   const uint16_t *q0 = p.q, *k0 = p.k, *v0 = p.v;
   uint16_t* o0 = p.o;
+  const float* q_rms0 = p.q_rms;
   p.ntq = (p.N + kBM - 1) / kBM;
   for (int b0 = 0; b0 < B; b0 += WANATTN_MAX_LEN_BATCH) {
     const int nb = B - b0 < WANATTN_MAX_LEN_BATCH ? B - b0 : WANATTN_MAX_LEN_BATCH;
@@ -305,6 +306,7 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
     p.k = k0 + (size_t)b0 * kstride;
     p.v = v0 + (size_t)b0 * kstride;
     p.o = o0 + (size_t)b0 * qstride;
+    if constexpr (QNORM) p.q_rms = q_rms0 + (size_t)b0 * p.N;
     for (int b = 0; b < nb; ++b) p.lens[b] = lens ? lens[b0 + b] : p.Nk;
     p.total = nb * p.heads * p.ntq;
     if constexpr (ROPE) {
@@ -322,7 +324,7 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
         p.queue = (unsigned*)((char*)part + part_items * kSplitItemBytes);
         hipLaunchKernelGGL(zero_queue_kernel, dim3(1), dim3(64), 0, stream, p.queue);
         WA_TRY(launched("queue reset"));
-        hipLaunchKernelGGL((attn_fwd_kernel<ROPE, CAUSAL, true>), dim3(ncu), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<ROPE, CAUSAL, true, QNORM>), dim3(ncu), dim3(kThreads), 0, stream, p);
         WA_TRY(launched("attention"));
         if (nsplit) {
           MergeParams m{p.part_o, p.part_lb, p.o, p.total, p.ntq, p.heads, p.N, nsplit};
@@ -344,7 +346,7 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
         continue;
       }
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<ROPE, CAUSAL>), dim3(p.total), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<ROPE, CAUSAL, false, QNORM>), dim3(p.total), dim3(kThreads), 0, stream, p);
     WA_TRY(launched("attention"));
   }
   return WANATTN_OK;
@@ -354,8 +356,10 @@ wanattn_status launch_attn(AttnParams p, int32_t B, const int32_t* lens, hipStre
 // tab + h * hstride); arguments already checked
 wanattn_status rope3d_launch(const void* x, void* y, int32_t B, int32_t N, int32_t heads,
                              const wanattn_grid3d* grid, const float2* tab, long long hstride,
-                             hipStream_t stream) {
+                             hipStream_t stream, const float* rms = nullptr, const void* gamma = nullptr) {
   RopeParams p;
+  p.rms = rms;
+  p.gamma = (const uint16_t*)gamma;
   p.x = (const u32x4*)x;
   p.y = (u32x4*)y;
   p.tab = tab;
@@ -435,13 +439,19 @@ wanattn_status check_self(const void* q, const void* k, const void* v, const voi
 
 // keys rotated once into kprime (with head h's table at tab + h * hstride);
 // the queries are rotated by the attention kernel as it loads them
+// (rms, gq, gk non-null: q and k are projections before the QK-Norm, whose
+// factors rms holds, q's then k's; the norm is applied as q is loaded and as k
+// is rotated)
 wanattn_status self_launch(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t N,
                            int32_t heads, const wanattn_grid3d* grid, float scale, wanattn_mask mask,
                            int32_t chunk_frames, const int32_t* kv_lens, void* kprime, const float2* tab,
-                           long long hstride, void* part, size_t part_items, hipStream_t stream) {
-  WA_TRY(rope3d_launch(k, kprime, B, N, heads, grid, tab, hstride, stream));
+                           long long hstride, void* part, size_t part_items, hipStream_t stream,
+                           const float* rms = nullptr, const void* gq = nullptr, const void* gk = nullptr) {
+  WA_TRY(rope3d_launch(k, kprime, B, N, heads, grid, tab, hstride, stream, rms ? rms + (size_t)B * N : nullptr, gk));
   AttnParams p;
   memset(&p, 0, sizeof p);
+  p.q_rms = rms;
+  p.gq = (const uint16_t*)gq;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)kprime;
   p.v = (const uint16_t*)v;
@@ -462,8 +472,10 @@ wanattn_status self_launch(const void* q, const void* k, const void* v, void* o,
   if (mask == WANATTN_MASK_BLOCK_CAUSAL) {
     long long ct = (long long)chunk_frames * grid->H * grid->W;
     p.chunk_tokens = (int)(ct < N ? ct : N);
+    if (rms) return launch_attn<true, true, true>(p, B, kv_lens, stream, part, part_items);
     return launch_attn<true, true>(p, B, kv_lens, stream, part, part_items);
   }
+  if (rms) return launch_attn<true, false, true>(p, B, kv_lens, stream, part, part_items);
   return launch_attn<true, false>(p, B, kv_lens, stream, part, part_items);
 }
 
@@ -658,6 +670,115 @@ wanattn_status gemm_plan(ProjDesc& pd, int dim, long long rows, hipblasLtHandle_
 }
 
 size_t prologue_y_bytes(long long rows, int dim) { return ((size_t)rows * dim * 2 + 255) & ~size_t(255); }
+
+// the prologue up to the projections, then either the QK RMSNorm in place
+// (rms null; gq, gk its weights) or only its per-row factors into rms
+wanattn_status prologue_core(const void* x, const float* e0, const float* e1, const void* wq, const void* bq,
+                             const void* wk, const void* bk, const void* wv, const void* bv, const void* gq,
+                             const void* gk, void* q, void* k, void* v, float* rms, int32_t B, int32_t N,
+                             int32_t dim, float eps_ln, float eps_rms, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  t_err[0] = 0;
+  const void* ins[11] = {x, e0, e1, wq, bq, wk, bk, wv, bv, rms ? x : gq, rms ? x : gk};
+  void* outs[3] = {q, k, v};
+  for (const void* a : ins)
+    if (!a) return fail(WANATTN_E_INVALID, "null input pointer");
+  if (rms && ((uintptr_t)rms & 15u) != 0) return fail(WANATTN_E_INVALID, "rms must be 16-byte aligned");
+  for (const void* a : outs)
+    if (!a) return fail(WANATTN_E_INVALID, "null output pointer");
+  for (const void* a : ins)
+    if (!aligned16(a)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  for (const void* a : outs)
+    if (!aligned16(a)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
+  if (B < 1 || N < 1) return fail(WANATTN_E_INVALID, "B and N must be >= 1");
+  if (dim < 8 || dim % 8 != 0) return fail(WANATTN_E_INVALID, "dim=%d must be a positive multiple of 8", dim);
+  if (dim > kMaxRowDim) return fail(WANATTN_E_UNSUPPORTED, "dim=%d above %d", dim, kMaxRowDim);
+  const long long rows = (long long)B * N;
+  if (rows > kMaxPrologueRows) return fail(WANATTN_E_UNSUPPORTED, "B*N=%lld above %lld tokens", rows, kMaxPrologueRows);
+  if (!(eps_ln >= 0.0f) || !std::isfinite(eps_ln) || !(eps_rms >= 0.0f) || !std::isfinite(eps_rms))
+    return fail(WANATTN_E_INVALID, "eps_ln and eps_rms must be finite and >= 0");
+  const size_t act = (size_t)rows * dim * 2, mat = (size_t)dim * dim * 2, vec = (size_t)dim * 2,
+               mod = (size_t)B * dim * 4;
+  const size_t in_bytes[11] = {act, mod, mod, mat, vec, mat, vec, mat, vec, vec, vec};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 11; ++j)
+      if (overlap(outs[i], act, ins[j], in_bytes[j])) return fail(WANATTN_E_INVALID, "an output overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], act, outs[j], act)) return fail(WANATTN_E_INVALID, "q, k and v overlap");
+  }
+  if (!workspace) return fail(WANATTN_E_INVALID, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(WANATTN_E_INVALID, "workspace must be 256-byte aligned");
+  const size_t need = prologue_y_bytes(rows, dim) + kGemmWorkspace;
+  if (workspace_bytes < need)
+    return fail(WANATTN_E_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  for (int j = 0; j < 11; ++j)
+    if (overlap(workspace, need, ins[j], in_bytes[j])) return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
+  for (int i = 0; i < 3; ++i)
+    if (overlap(workspace, need, outs[i], act)) return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
+  if (rms) {
+    const size_t rbytes = (size_t)rows * 2 * sizeof(float);
+    for (int j = 0; j < 11; ++j)
+      if (overlap(rms, rbytes, ins[j], in_bytes[j])) return fail(WANATTN_E_INVALID, "rms overlaps an input");
+    for (int i = 0; i < 3; ++i)
+      if (overlap(rms, rbytes, outs[i], act)) return fail(WANATTN_E_INVALID, "rms overlaps an output");
+    if (overlap(rms, rbytes, workspace, need)) return fail(WANATTN_E_INVALID, "rms overlaps the workspace");
+  }
+
+  ProjDesc pd;
+  WA_TRY(pd.init(dim, rows));
+  hipblasLtHandle_t h = nullptr;
+  GemmPlan plan;
+  WA_TRY(gemm_plan(pd, dim, rows, &h, &plan));
+  const hipStream_t st = (hipStream_t)stream;
+  uint16_t* y = (uint16_t*)workspace;
+  void* gemm_ws = (char*)workspace + prologue_y_bytes(rows, dim);
+
+  LnModParams lp;
+  lp.x = (const uint16_t*)x;
+  lp.e0 = e0;
+  lp.e1 = e1;
+  lp.y = y;
+  lp.rows = rows;
+  lp.N = N;
+  lp.dim = dim;
+  lp.eps = eps_ln;
+  hipError_t le = launch_rows<LnModLaunch>(dim, dim3((unsigned)((rows + 3) / 4)), st, lp);
+  if (le != hipSuccess) return fail(WANATTN_E_HIP, "ln_mod launch: %s", hipGetErrorString(le));
+
+  const float one = 1.0f, zero = 0.0f;
+  const void* w[3] = {wq, wk, wv};
+  const void* bias[3] = {bq, bk, bv};
+  for (int i = 0; i < 3; ++i) {
+    WA_TRY(pd.set_bias(bias[i]));
+    LT_TRY(hipblasLtMatmul(h, pd.op, &one, w[i], pd.a, y, pd.b, &zero, outs[i], pd.d, outs[i], pd.d, &plan.algo,
+                           gemm_ws, plan.ws, st),
+           "projection GEMM");
+  }
+
+  if (rms) {
+    RmsStatParams sp;
+    sp.q = (const uint16_t*)q;
+    sp.k = (const uint16_t*)k;
+    sp.rms = rms;
+    sp.rows = rows;
+    sp.dim = dim;
+    sp.eps = eps_rms;
+    le = launch_rows<QkRmsStatLaunch>(dim, dim3((unsigned)((2 * rows + 3) / 4)), st, sp);
+    if (le != hipSuccess) return fail(WANATTN_E_HIP, "qk_rms_stats launch: %s", hipGetErrorString(le));
+    return WANATTN_OK;
+  }
+  RmsParams rp;
+  rp.q = (uint16_t*)q;
+  rp.k = (uint16_t*)k;
+  rp.gq = (const uint16_t*)gq;
+  rp.gk = (const uint16_t*)gk;
+  rp.rows = rows;
+  rp.dim = dim;
+  rp.eps = eps_rms;
+  le = launch_rows<QkRmsLaunch>(dim, dim3((unsigned)((2 * rows + 3) / 4)), st, rp);
+  if (le != hipSuccess) return fail(WANATTN_E_HIP, "qk_rmsnorm launch: %s", hipGetErrorString(le));
+  return WANATTN_OK;
+}
 
 }  // namespace
 
@@ -873,85 +994,50 @@ wanattn_status wanattn_prologue(const void* x, const float* e0, const float* e1,
                                 void* v, int32_t B, int32_t N, int32_t dim, float eps_ln,
                                 float eps_rms, void* workspace, size_t workspace_bytes,
                                 void* stream) {
+  return prologue_core(x, e0, e1, wq, bq, wk, bk, wv, bv, gq, gk, q, k, v, nullptr, B, N, dim, eps_ln, eps_rms,
+                       workspace, workspace_bytes, stream);
+}
+
+wanattn_status wanattn_prologue_rms(const void* x, const float* e0, const float* e1, const void* wq,
+                                    const void* bq, const void* wk, const void* bk, const void* wv,
+                                    const void* bv, void* q, void* k, void* v, float* rms, int32_t B,
+                                    int32_t N, int32_t dim, float eps_ln, float eps_rms, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!rms) {
+    t_err[0] = 0;
+    return fail(WANATTN_E_INVALID, "rms is NULL");
+  }
+  return prologue_core(x, e0, e1, wq, bq, wk, bk, wv, bv, nullptr, nullptr, q, k, v, rms, B, N, dim, eps_ln,
+                       eps_rms, workspace, workspace_bytes, stream);
+}
+
+wanattn_status wanattn_self_qknorm(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t N,
+                                   int32_t heads, int32_t head_dim, const wanattn_grid3d* grid, double theta,
+                                   float scale, wanattn_mask mask, int32_t chunk_frames, const int32_t* kv_lens,
+                                   const float* rms, const void* gq, const void* gk, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
   t_err[0] = 0;
-  const void* ins[11] = {x, e0, e1, wq, bq, wk, bk, wv, bv, gq, gk};
-  void* outs[3] = {q, k, v};
-  for (const void* a : ins)
-    if (!a) return fail(WANATTN_E_INVALID, "null input pointer");
-  for (const void* a : outs)
-    if (!a) return fail(WANATTN_E_INVALID, "null output pointer");
-  for (const void* a : ins)
-    if (!aligned16(a)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
-  for (const void* a : outs)
-    if (!aligned16(a)) return fail(WANATTN_E_INVALID, "tensors must be 16-byte aligned");
-  if (B < 1 || N < 1) return fail(WANATTN_E_INVALID, "B and N must be >= 1");
-  if (dim < 8 || dim % 8 != 0) return fail(WANATTN_E_INVALID, "dim=%d must be a positive multiple of 8", dim);
-  if (dim > kMaxRowDim) return fail(WANATTN_E_UNSUPPORTED, "dim=%d above %d", dim, kMaxRowDim);
-  const long long rows = (long long)B * N;
-  if (rows > kMaxPrologueRows) return fail(WANATTN_E_UNSUPPORTED, "B*N=%lld above %lld tokens", rows, kMaxPrologueRows);
-  if (!(eps_ln >= 0.0f) || !std::isfinite(eps_ln) || !(eps_rms >= 0.0f) || !std::isfinite(eps_rms))
-    return fail(WANATTN_E_INVALID, "eps_ln and eps_rms must be finite and >= 0");
-  const size_t act = (size_t)rows * dim * 2, mat = (size_t)dim * dim * 2, vec = (size_t)dim * 2,
-               mod = (size_t)B * dim * 4;
-  const size_t in_bytes[11] = {act, mod, mod, mat, vec, mat, vec, mat, vec, vec, vec};
-  for (int i = 0; i < 3; ++i) {
-    for (int j = 0; j < 11; ++j)
-      if (overlap(outs[i], act, ins[j], in_bytes[j])) return fail(WANATTN_E_INVALID, "an output overlaps an input");
-    for (int j = i + 1; j < 3; ++j)
-      if (overlap(outs[i], act, outs[j], act)) return fail(WANATTN_E_INVALID, "q, k and v overlap");
-  }
-  if (!workspace) return fail(WANATTN_E_INVALID, "workspace is NULL");
-  if (((uintptr_t)workspace & 255u) != 0) return fail(WANATTN_E_INVALID, "workspace must be 256-byte aligned");
-  const size_t need = prologue_y_bytes(rows, dim) + kGemmWorkspace;
-  if (workspace_bytes < need)
-    return fail(WANATTN_E_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  for (int j = 0; j < 11; ++j)
-    if (overlap(workspace, need, ins[j], in_bytes[j])) return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
-  for (int i = 0; i < 3; ++i)
-    if (overlap(workspace, need, outs[i], act)) return fail(WANATTN_E_INVALID, "workspace overlaps a tensor");
-
-  ProjDesc pd;
-  WA_TRY(pd.init(dim, rows));
-  hipblasLtHandle_t h = nullptr;
-  GemmPlan plan;
-  WA_TRY(gemm_plan(pd, dim, rows, &h, &plan));
-  const hipStream_t st = (hipStream_t)stream;
-  uint16_t* y = (uint16_t*)workspace;
-  void* gemm_ws = (char*)workspace + prologue_y_bytes(rows, dim);
-
-  LnModParams lp;
-  lp.x = (const uint16_t*)x;
-  lp.e0 = e0;
-  lp.e1 = e1;
-  lp.y = y;
-  lp.rows = rows;
-  lp.N = N;
-  lp.dim = dim;
-  lp.eps = eps_ln;
-  hipError_t le = launch_rows<LnModLaunch>(dim, dim3((unsigned)((rows + 3) / 4)), st, lp);
-  if (le != hipSuccess) return fail(WANATTN_E_HIP, "ln_mod launch: %s", hipGetErrorString(le));
-
-  const float one = 1.0f, zero = 0.0f;
-  const void* w[3] = {wq, wk, wv};
-  const void* bias[3] = {bq, bk, bv};
-  for (int i = 0; i < 3; ++i) {
-    WA_TRY(pd.set_bias(bias[i]));
-    LT_TRY(hipblasLtMatmul(h, pd.op, &one, w[i], pd.a, y, pd.b, &zero, outs[i], pd.d, outs[i], pd.d, &plan.algo,
-                           gemm_ws, plan.ws, st),
-           "projection GEMM");
-  }
-
-  RmsParams rp;
-  rp.q = (uint16_t*)q;
-  rp.k = (uint16_t*)k;
-  rp.gq = (const uint16_t*)gq;
-  rp.gk = (const uint16_t*)gk;
-  rp.rows = rows;
-  rp.dim = dim;
-  rp.eps = eps_rms;
-  le = launch_rows<QkRmsLaunch>(dim, dim3((unsigned)((2 * rows + 3) / 4)), st, rp);
-  if (le != hipSuccess) return fail(WANATTN_E_HIP, "qk_rmsnorm launch: %s", hipGetErrorString(le));
-  return WANATTN_OK;
+  WA_TRY(check_theta(theta));
+  WA_TRY(check_self_args(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens));
+  if (!rms || !gq || !gk) return fail(WANATTN_E_INVALID, "rms, gq and gk must be given");
+  if (((uintptr_t)rms & 3u) != 0 || !aligned16(gq) || !aligned16(gk))
+    return fail(WANATTN_E_INVALID, "rms must be 4-byte and gq, gk 16-byte aligned");
+  const size_t bytes = (size_t)B * N * heads * kHeadDim * 2;
+  const size_t rbytes = (size_t)B * N * 2 * sizeof(float), gbytes = (size_t)heads * kHeadDim * 2;
+  if (overlap(o, bytes, rms, rbytes) || overlap(o, bytes, gq, gbytes) || overlap(o, bytes, gk, gbytes))
+    return fail(WANATTN_E_INVALID, "o overlaps rms or a gamma");
+  const size_t items = split_items(B, N, heads), full = bytes + items * kSplitItemBytes + kQueueBytes;
+  const bool room = workspace_bytes >= full;
+  WA_TRY(check_self(q, k, v, o, B, N, heads, head_dim, grid, scale, mask, chunk_frames, kv_lens, workspace,
+                    workspace_bytes, bytes, room ? full : bytes));
+  const size_t ws_use = room ? full : bytes;
+  if (overlap(workspace, ws_use, rms, rbytes) || overlap(workspace, ws_use, gq, gbytes) ||
+      overlap(workspace, ws_use, gk, gbytes))
+    return fail(WANATTN_E_INVALID, "workspace overlaps rms or a gamma");
+  const float2* tab = nullptr;
+  WA_TRY(table_for(theta, (hipStream_t)stream, &tab));
+  return self_launch(q, k, v, o, B, N, heads, grid, scale, mask, chunk_frames, kv_lens, workspace, tab, 0,
+                     room ? (char*)workspace + bytes : nullptr, room ? items : 0, (hipStream_t)stream, rms, gq, gk);
 }
 
 }  // extern "C"

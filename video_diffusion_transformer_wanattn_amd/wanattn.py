@@ -26,7 +26,8 @@ EXPORTS = ("wanattn_rope3d", "wanattn_self", "wanattn_self_workspace_bytes", "wa
            "wanattn_self_jitter_workspace_bytes", "wanattn_self_kv", "wanattn_rope_tables_bytes",
            "wanattn_rope_tables", "wanattn_rope3d_tables", "wanattn_self_kv_tables",
            "wanattn_cross", "wanattn_prologue", "wanattn_prologue_workspace_bytes", "wanattn_prepare",
-           "wanattn_status_string", "wanattn_last_error", "wanattn_version", "wanattn_self_noalloc")
+           "wanattn_status_string", "wanattn_last_error", "wanattn_version", "wanattn_self_noalloc",
+           "wanattn_prologue_rms", "wanattn_self_qknorm")
 
 NOALLOC_SCRATCH_BYTES = 512 << 20
 
@@ -85,6 +86,11 @@ def load_library(path: str = LIB_PATH):
     lib.wanattn_cross.restype = ctypes.c_int
     lib.wanattn_prologue.argtypes = [P] * 14 + [i32, i32, i32, f32, f32, P, ctypes.c_size_t, P]
     lib.wanattn_prologue.restype = ctypes.c_int
+    lib.wanattn_prologue_rms.argtypes = [P] * 13 + [i32, i32, i32, f32, f32, P, ctypes.c_size_t, P]
+    lib.wanattn_prologue_rms.restype = ctypes.c_int
+    lib.wanattn_self_qknorm.argtypes = [P, P, P, P, i32, i32, i32, i32, G, f64, f32, ctypes.c_int, i32, P,
+                                        P, P, P, P, ctypes.c_size_t, P]
+    lib.wanattn_self_qknorm.restype = ctypes.c_int
     lib.wanattn_prologue_workspace_bytes.argtypes = [i32, i32, i32]
     lib.wanattn_prologue_workspace_bytes.restype = ctypes.c_size_t
     lib.wanattn_prepare.argtypes = [f64]
@@ -394,6 +400,81 @@ def prologue(x, e0, e1, wq, bq, wk, bk, wv, bv, gq, gk, eps_ln: float = 1e-6, ep
                                    _ptr(out[2]), B, N, dim, float(eps_ln), float(eps_rms),
                                    _ptr(workspace), ws_bytes, _stream(stream)))
     return tuple(out)
+
+
+def prologue_rms(x, e0, e1, wq, bq, wk, bk, wv, bv, eps_ln: float = 1e-6, eps_rms: float = 1e-6,
+                 out=None, rms=None, workspace=None, stream=None):
+    """prologue() with the QK-Norm left to self_attention_qknorm: returns (q, k,
+    v, rms) with q and k before the RMSNorm and rms a float32 [2, B * N] tensor
+    of the RMSNorm factors (q's row, then k's)."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, dim]")
+    B, N, dim = (int(a) for a in x.shape)
+    with _on(stream):
+        if out is None:
+            out = tuple(torch.empty_like(x) for _ in range(3))
+        if rms is None:
+            rms = torch.empty(2, B * N, dtype=torch.float32, device=x.device)
+    for t in (x, *out, wq, wk, wv, bq, bk, bv):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("x, weights, biases and outputs must be contiguous bf16 GPU tensors")
+    for t in (e0, e1):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, dim):
+            raise ValueError("e0 and e1 must be contiguous float32 GPU tensors [B, dim]")
+    if not rms.is_cuda or rms.dtype != torch.float32 or not rms.is_contiguous() or rms.numel() != 2 * B * N:
+        raise ValueError("rms must be a contiguous float32 GPU tensor of 2 * B * N values")
+    if any(tuple(t.shape) != (B, N, dim) for t in out):
+        raise ValueError("outputs must be [B, N, dim]")
+    if any(tuple(t.shape) != (dim, dim) for t in (wq, wk, wv)) or any(tuple(t.shape) != (dim,) for t in (bq, bk, bv)):
+        raise ValueError("weights must be [dim, dim] and biases [dim]")
+    need = int(lib.wanattn_prologue_workspace_bytes(B, N, dim))
+    if workspace is None:
+        with _on(stream):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _raise_on(lib.wanattn_prologue_rms(_ptr(x), _ptr(e0), _ptr(e1), _ptr(wq), _ptr(bq), _ptr(wk), _ptr(bk),
+                                       _ptr(wv), _ptr(bv), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(rms),
+                                       B, N, dim, float(eps_ln), float(eps_rms), _ptr(workspace), ws_bytes,
+                                       _stream(stream)))
+    return (*out, rms)
+
+
+def self_attention_qknorm(q, k, v, rms, gq, gk, grid, theta: float = 10000.0, scale: float | None = None,
+                          block_causal: bool = False, chunk_frames: int = 3, kv_lens=None, offsets=(0, 0, 0),
+                          out=None, workspace=None, stream=None):
+    """self_attention on prologue_rms's outputs: q and k before the QK-Norm
+    ([B, N, heads, 128] bf16), rms its factors, gq and gk its weights
+    ([heads * 128] bf16); the norm is applied as q is loaded and k rotated."""
+    import torch
+    lib = load_library()
+    if out is None:
+        with _on(stream):
+            out = torch.empty_like(q)
+    B, N, heads, d = _dims(q, k, v, out)
+    if not (tuple(k.shape) == tuple(v.shape) == tuple(out.shape) == tuple(q.shape)):
+        raise ValueError("q, k, v and out must have the same shape")
+    if not rms.is_cuda or rms.dtype != torch.float32 or not rms.is_contiguous() or rms.numel() != 2 * B * N:
+        raise ValueError("rms must be a contiguous float32 GPU tensor of 2 * B * N values")
+    for g in (gq, gk):
+        if not g.is_cuda or g.dtype != torch.bfloat16 or not g.is_contiguous() or g.numel() != heads * d:
+            raise ValueError("gq and gk must be contiguous bf16 GPU tensors of heads * head_dim values")
+    if kv_lens is not None and len(kv_lens) != B:
+        raise ValueError("kv_lens needs one entry per batch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = int(lib.wanattn_self_workspace_bytes(B, N, heads, d))
+    if workspace is None:
+        with _on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    mask = MASK_BLOCK_CAUSAL if block_causal else MASK_NONE
+    _raise_on(lib.wanattn_self_qknorm(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, heads, d,
+                                      ctypes.byref(_grid(grid, offsets)), float(theta), float(scale), mask,
+                                      int(chunk_frames), _lens(kv_lens, B), _ptr(rms), _ptr(gq), _ptr(gk),
+                                      _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
 
 
 def prepare(theta: float = 10000.0):

@@ -228,7 +228,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
   // fixed item order of the prefetching launch: workgroup w (of 8 c, run on XCD
   // w % 8) takes items w / 8, w / 8 + c, ... of XCD w % 8's contiguous run
   int pass = 0;
-  bool pre = false;   // this pass's first two tiles and its queries were loaded last pass
+  // this pass's queries (qpre) and first two tiles (tpre) were loaded last pass
+  bool qpre = false, tpre = false;
   auto static_item = [&](const auto& pp, int ps) -> int {
     const int x = blockIdx.x & 7, j = blockIdx.x >> 3, c = gridDim.x >> 3;
     const int per = pp.total >> 3, rem = pp.total & 7;
@@ -367,18 +368,42 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
       }
     };
 
+    // (prefetching launch) this wave's 64 query rows of query tile tq_ of
+    // (batch bq, head hq) into LDS at prefetch_q_base(wave): instruction i fills
+    // rows 4 i + lane / 16, stored chunk lane % 16 holding chunk (lane % 16) ^
+    // (row & 15).  Rows past the last token repeat it; a wave whose rows all lie
+    // past it (a partial last tile) reads the last token's row: the load base is
+    // the wave's first row clamped, so every offset is 0..63 rows.
+    auto dma_q = [&](int bq, int hq, int tq_) __attribute__((always_inline)) {
+      const int ibase = tq_ * kBM + wave * 64;
+      const int ib0 = min(ibase, p.N - 1);
+      const char* qn = (const char*)(p.q + (((size_t)bq * p.N + ib0) * p.heads + hq) * kHeadDim);
+      const uint32_t qst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds + prefetch_q_base(wave));
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 4 * i + ld_row;
+        const int rowc = min(ibase + row, p.N - 1) - ib0;
+        dma16(qn, (uint32_t)rowc * rsb + 16 * (ld_chunk ^ (row & 15)), qst + i * 1024);
+      }
+    };
     // the look-ahead scoring of the block after the last one reads the next
     // stage: with fewer tiles than stages that stage was never filled, so zero
     // the stages then (with more, it holds an earlier tile: finite values whose
     // scores are discarded).  nt is uniform over the workgroup.
-    if (!(PREFETCH && pre)) {
-      if (nt < kStages) {
+    auto zero_stages = [&]() __attribute__((always_inline)) {
   #pragma unroll
-        for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i)
-          *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < kLdsBytes / 16 / kThreads; ++i)
+        *(u32x4*)(lds + 16 * (tid + i * kThreads)) = u32x4{0, 0, 0, 0};
+    };
+    if constexpr (PREFETCH) {
+      // the queries always come through LDS: loaded last pass, else now (the
+      // first pass); the tiles follow the query reads when not prefetched
+      if (!qpre) dma_q(b, head, tq);
+    } else {
+      if (nt < kStages) {
+        zero_stages();
         tile_barrier();
       }
-
       // prefetch the first two tiles while the queries are loaded
       issue_tile(S0{}, 0);
       if (nt > 1) issue_tile(S1{}, 1);
@@ -407,11 +432,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         pw[qb] = w + p.w0;
       }
       const u32x4* src = (const u32x4*)(qbase + (size_t)ic * row_stride);
-      if (PREFETCH && pre) {
-        // from LDS, where this wave's own loads put its rows last pass (row
-        // rho's chunk c stored at c ^ (rho & 15)); only the output stores of
-        // the last epilogue may still be outstanding
-        if (qb == 0) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      if constexpr (PREFETCH) {
+        // from LDS, where this wave's own loads put its rows (row rho's chunk c
+        // stored at c ^ (rho & 15)).  The wait is for every outstanding vector
+        // memory operation, the last epilogue's output stores included: a store
+        // can complete before a load issued ahead of it, so a count that leaves
+        // the stores outstanding does not prove the loads done (with vmcnt(16),
+        // rows of some waves were read before their loads landed).  No global
+        // load of q exists in this kernel (a path that could leave one in
+        // flight to these registers made the compiler wait before each read).
+        if (qb == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const int rho = qb * 32 + r;
         const char* qrow = lds + prefetch_q_base(wave) + rho * kRowBytes;
   #pragma unroll
@@ -641,10 +671,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
       asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
     };
 
+    if constexpr (PREFETCH) {
+      if (!tpre) {
+        // every wave has read its queries, which lie in stages 2 and 3
+        if (nt < kStages) {
+          tile_barrier();
+          zero_stages();
+          tile_barrier();
+        }
+        issue_tile(S0{}, 0);
+        if (nt > 1) issue_tile(S1{}, 1);
+      }
+    }
     // ---- prologue: tile 0 resident, tile 2 requested, block 0 scored and
     // finished, K' operands of block 1 loaded (prefetched tiles are resident
     // since the wait for the prefetched queries, which were loaded after them)
-    if (!(PREFETCH && pre)) {
+    if (!(PREFETCH && tpre)) {
       if (nt > 1) wait_vm<8>();
       else wait_vm<0>();
     }
@@ -690,16 +732,24 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     // t+3 is full, and need no element mask.
     auto block_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t, int kb) __attribute__((always_inline)) {
       const int j = 2 * t + kb;
-      if constexpr (!decltype(MASKED)::value) {
+      // (prefetched tiles: at tile 0, tile 1 is resident since the item's
+      // first wait, for all outstanding loads, and the barrier after it, and
+      // every wave has read its queries from stages 2 and 3)
+      const bool first_ready = PREFETCH && tpre && t == 0;
+      // (clean items' last tiles: past the last tile, the last tile again; see clean below)
+      const int tn = decltype(MASKED)::value == 2 ? min(t + 3, nt - 1) : t + 3;
+      if constexpr (decltype(MASKED)::value != 1) {
         // the loads of tile t+3 are spread over the QK^T groups below
-        if (kb == 0) {
+        if (kb == 0 && !first_ready) {
           wait_vm<8>();
           tile_barrier();
         }
       } else if (kb == 0 && t + 1 < nt) {
-        if (t + 2 < nt) wait_vm<8>();
-        else wait_vm<0>();
-        tile_barrier();
+        if (!first_ready) {
+          if (t + 2 < nt) wait_vm<8>();
+          else wait_vm<0>();
+          tile_barrier();
+        }
         if (t + 3 < nt) issue_tile(SNN, t + 3);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -719,8 +769,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         // and would otherwise be sunk past it
         asm volatile("" : "+v"(pk1[kk >> 2][kk & 3]));
         load_vop(S, kb, kk >> 1, kk & 1);
-        if constexpr (!decltype(MASKED)::value) {
-          if (kb == 0) issue_one(SNN, t + 3, kk);
+        if constexpr (decltype(MASKED)::value != 1) {
+          if (kb == 0) issue_one(SNN, tn, kk);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -761,7 +811,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         if (g == 0) {
           take_scores();
           // (tail tiles: only blocks that reach past a row's visible keys)
-          if constexpr (decltype(MASKED)::value)
+          if constexpr (decltype(MASKED)::value == 1)
             if (32 * (j + 1) + 32 > kv_full) mask_scores(j + 1);
         }
         // the exps after this product, not hoisted above it (the two products
@@ -788,8 +838,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         scar[qb] = h0[qb][0] + h0[qb][1];
       }
     };
-    using NoMask = std::integral_constant<bool, false>;
-    using Mask = std::integral_constant<bool, true>;
+    // step kinds: unmasked, masked (run-time checks of which tiles exist), and
+    // unmasked with the load of tile t+3 clamped to the last tile
+    using NoMask = std::integral_constant<int, 0>;
+    using Mask = std::integral_constant<int, 1>;
+    using Clamp = std::integral_constant<int, 2>;
     // Block j+1 (scored in step j) needs the element mask iff 32 (j+1) + 32 > kv_full,
     // i.e. from block jm = kv_full / 32 on.  Whole tiles whose steps score only
     // earlier blocks, and for which tile t+3 exists and is full, run in the
@@ -797,6 +850,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     // the chunk a causal query tile straddles) run in a loop with run-time stages.
     const int jm = kv_full / 32;
     const int tm = max(0, min(min(nt, (jm - 1) / 2), Nk / kBN - 3));
+    // A clean item (every visible key of every row in whole tiles: no causal
+    // straddle, kv_end a multiple of kBN, at least kStages tiles) runs its last
+    // tiles unmasked too, four at a time: those steps load the last tile again
+    // into the stage that would take a tile past the last (one every wave has
+    // left; only the discarded look-ahead block past the last reads it), so that
+    // every tile start waits on the same count.  Cross attention over 512 text
+    // keys is one; only its kernel has this copy of the step (in the main loop
+    // the clamp cost register moves, and self attention's tails are short).
+    const bool clean = kv_full == kv_end && kv_end == nt * kBN && nt >= kStages;
     auto tile_step = [&](auto S, auto SN, auto SNN, auto MASKED, int t) __attribute__((always_inline)) {
       block_step(S, SN, SNN, MASKED, t, 0);
       block_step(S, SN, SNN, MASKED, t, 1);
@@ -820,8 +882,41 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
       tile_step(S2{}, S3{}, S1{}, NoMask{}, t + 2);
       tile_step(S3{}, S0{}, S2{}, NoMask{}, t + 3);
     }
+    if constexpr (PREFETCH) {
+      if (clean) {
+        for (; t + 4 <= nt; t += 4) {
+          tile_step(S0{}, S1{}, S3{}, Clamp{}, t);
+          tile_step(S1{}, S2{}, S0{}, Clamp{}, t + 1);
+          tile_step(S2{}, S3{}, S1{}, Clamp{}, t + 2);
+          tile_step(S3{}, S0{}, S2{}, Clamp{}, t + 3);
+        }
+      }
+    }
     for (; t < nt; ++t) tile_step(t, t + 1, t + 3, Mask{}, t);
 
+    // 32 staged output rows (row m's chunk c at c ^ (m & 15), 256 bytes a row)
+    // to O: lane (sr, sc) = (lane / 16, lane % 16) writes chunk sc of rows
+    // 4 it + sr, 1 KiB (4 whole rows) per instruction.  All reads are issued
+    // before the stores; a block that reaches past the last token checks each
+    // row.  (irow0: the token of row sr)
+    auto store_rows = [&](const char* rows, uint16_t* dst, bool whole, int irow0) __attribute__((always_inline)) {
+      const int sr = lane >> 4, sc = lane & 15;
+      u32x4 w[8];
+  #pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = 4 * it + sr;
+        w[it] = *(const u32x4*)(rows + row * kRowBytes + 16 * (sc ^ (row & 15)));
+      }
+      const size_t step = 4 * ((size_t)p.heads * kHeadDim);
+      if (whole) {
+  #pragma unroll
+        for (int it = 0; it < 8; ++it) *(u32x4*)(dst + it * step) = w[it];
+      } else {
+  #pragma unroll
+        for (int it = 0; it < 8; ++it)
+          if (irow0 + 4 * it < p.N) *(u32x4*)(dst + it * step) = w[it];
+      }
+    };
     if (split) {
       // ---- partial epilogue: O, l and the bias as they stand, fp32, one
       // whole 1 KiB run of float4 per store instruction
@@ -855,7 +950,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     if constexpr (PREFETCH) {
       // the next item's first two tiles (into stages 0 and 1, which every
       // wave has left) and its query loads, issued before this epilogue
-      pre = false;
+      qpre = tpre = false;
       const int Ln = static_item(p, pass + 1);
       if (Ln >= 0) {
         const int bhn = Ln / p.ntq, tqn = Ln - bhn * p.ntq;
@@ -878,23 +973,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
             dma16(kn + (size_t)kBN * rsb, koff_ld[i], st1 + blk * 1024);
             dma16(vn + (size_t)kBN * rsb, voff_ld[i], st1 + kVHalves + blk * 1024);
           }
-          // this wave's 64 query rows: instruction i fills rows 4 i + lane / 16,
-          // stored chunk lane % 16 holding chunk (lane % 16) ^ (row & 15)
-          // (rows past the last token repeat it; a wave whose rows all lie past
-          // it, in a partial last tile, reads the last token's row: the load
-          // base is the wave's first row clamped, so every offset is 0..63 rows)
-          const int ibase = tqn * kBM + wave * 64;
-          const int ib0 = min(ibase, p.N - 1);
-          const char* qn = (const char*)(p.q + (((size_t)bn * p.N + ib0) * p.heads + headn) * kHeadDim);
-          const uint32_t qst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds + prefetch_q_base(wave));
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = 4 * i + ld_row;
-            const int rowc = min(ibase + row, p.N - 1) - ib0;
-            dma16(qn, (uint32_t)rowc * rsb + 16 * (ld_chunk ^ (row & 15)), qst + i * 1024);
-          }
-          pre = true;
+          tpre = true;
         }
+        dma_q(bn, headn, tqn);
+        qpre = true;
       }
       ++pass;
     }
@@ -915,14 +997,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
             *(u32x2*)(orows + r * kRowBytes + 16 * ((4 * db + g4) ^ (r & 15)) + 8 * hh) = w;
           }
         const int irow0 = i0 + wave * 64 + qb * 32 + sr;
-        uint16_t* dst = p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc;
-  #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int row = 4 * it + sr;
-          const u32x4 w = *(const u32x4*)(orows + row * kRowBytes + 16 * (sc ^ (row & 15)));
-          if (irow0 + 4 * it < p.N) *(u32x4*)dst = w;
-          dst += 4 * row_stride;
-        }
+        store_rows(orows, p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc,
+                   i0 + wave * 64 + qb * 32 + 32 <= p.N, irow0);
       }
       continue;
     }
@@ -942,14 +1018,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
         }
     }
     const int sr = lane >> 4, sc = lane & 15;
-    const int irow0 = i0 + wave * 64 + sr;
-    uint16_t* dst = p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc;
   #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int row = 4 * it + sr;
-      const u32x4 w = *(const u32x4*)(orows + row * kRowBytes + 16 * (sc ^ (row & 15)));
-      if (irow0 + 4 * it < p.N) *(u32x4*)dst = w;
-      dst += 4 * row_stride;
+    for (int hf = 0; hf < 2; ++hf) {
+      const int irow0 = i0 + wave * 64 + 32 * hf + sr;
+      store_rows(orows + 32 * hf * kRowBytes,
+                 p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc,
+                 i0 + wave * 64 + 32 * hf + 32 <= p.N, irow0);
     }
     if constexpr (!PERSIST) break;
   }

@@ -19,6 +19,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -425,8 +426,8 @@ def metric_points(torch, seeded, wa, wl_main, main_tflops, main_ms, steps, warmu
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan14b_720p_81f")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -553,12 +554,18 @@ def main():
                      "traffic": measured_traffic(wl.name), "kernel": "attn_fwd_kernel (wanattn_self)",
                      "flops_per_launch": f_self},
         "self_ms": round(self_avg, 3),
+        "self_ms_median": round(statistics.median(self_ms), 3),
         "self_ms_min": round(min(self_ms), 3),
         "self_tflops": round(achieved, 2),
         "cross_ms": round(cross_avg, 4),
+        "cross_ms_median": round(statistics.median(cross_ms), 4),
+        "cross_ms_min": round(min(cross_ms), 4),
         "cross_tflops": round(f_cross / (cross_avg * 1e-3) / 1e12, 2),
         "cross_gbs": round(cross_bytes / (cross_avg * 1e-3) / 1e9, 1),
         "cross_frac_hbm": round(cross_bytes / (cross_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "cross_frac_mfma": round(f_cross / (cross_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        # the binding roof is the larger of the two times at peak
+        "cross_bound": "mfma" if f_cross / PEAK_BF16_TFLOPS / 1e12 >= cross_bytes / PEAK_HBM_GBS / 1e9 else "hbm",
     }
     if args.kv_stream:
         result["kv_stream"] = kv_stream_leg(torch, seeded, wa, args.steps, args.warmup)

@@ -23,11 +23,15 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("M,lens,N", [(512, [512, 100], 4096), (512, None, 4096), (77, [77, 1], 4096),
-                                       (300, [300, 193], 4096), (512, [512, 300], 3996)])
+                                       (300, [300, 193], 4096), (512, [512, 300], 3996),
+                                       (640, [640, 256], 4096), (512, [320, 448], 4096)])
 def test_cross_persistent_every_row(M, lens, N):
     # 2 x 16 x 16 = 512 query tiles: the persistent launch on a 256-CU chip;
     # N = 3996 leaves the last tile of every head with 156 rows, so its last
-    # two waves' rows all lie past the last token (their query loads repeat it)
+    # two waves' rows all lie past the last token (their query loads repeat it).
+    # Text lengths that are whole 64-key tiles (256, 320, 448, 512, 640) run
+    # their last tiles unmasked: 4 tiles (256) only there, 10 tiles (640) and
+    # 5 or 7 tiles (320, 448) with a masked remainder after them
     B, heads = 2, 16
     q = seeded.normal_bf16((B, N, heads, 128), 1400 + M + N, 1, 0.5)
     kc = seeded.normal_bf16((B, M, heads, 128), 1400 + M, 2, 0.5)

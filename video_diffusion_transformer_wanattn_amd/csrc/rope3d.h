@@ -5,9 +5,13 @@
 // and width segments of the head (44/42/42 wide) and multiplies q or k by them
 // as complex numbers.
 //
-// Memory-bound: one thread rotates one 16-byte chunk (4 complex pairs);
-// consecutive threads cover consecutive chunks, so loads and stores are fully
-// coalesced.  Bytes moved per element: 2 read + 2 written.
+// Memory-bound: a thread takes one 16-byte chunk (4 complex pairs) of one
+// token and rotates it in every head: the token's (f, h, w) and the chunk's
+// four (cos, sin) pairs are found once (with per-head tables, per head) and
+// the heads' chunks are then loaded, rotated and stored.  16 consecutive
+// threads cover one 256-byte head vector of a token, so every load and store
+// instruction moves whole 256-byte runs.  Bytes moved per element: 2 read + 2
+// written.
 #pragma once
 
 #include "common.h"
@@ -23,41 +27,53 @@ struct RopeParams {
   // row] * gamma[head * 128 + d], rms indexed by b * N + n
   const float* rms;
   const uint16_t* gamma;
-  long long chunks;  // B * N * heads * 16
+  long long chunks;  // B * N * 16: (token, 16-byte chunk) pairs
   int N, heads, H, W;
   int f0, h0, w0;
   double inv_hw, inv_w;
 };
 
 __global__ void __launch_bounds__(256) rope3d_kernel(RopeParams p) {
-  long long stride = (long long)gridDim.x * blockDim.x;
+  const long long stride = (long long)gridDim.x * blockDim.x;
   for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < p.chunks; idx += stride) {
-    int dc = (int)(idx & 15);                       // 16-byte chunk in the head vector
-    long long tok_head = idx >> 4;
-    const long long tok = tok_head / p.heads;
-    int n = (int)(tok % p.N);                       // token index in its batch
-    const float2* tab = p.tab + (tok_head - tok * p.heads) * p.tab_hstride;
+    const int dc = (int)(idx & 15);                 // 16-byte chunk in the head vector
+    const unsigned tok = (unsigned)(idx >> 4);      // b * N + n (fewer than 2^31 tokens fit in memory)
+    const int n = (int)(tok % (unsigned)p.N);       // token index in its batch
     int f, rem, h, w;
     divmod(n, p.H * p.W, p.inv_hw, f, rem);
     divmod(rem, p.W, p.inv_w, h, w);
-    u32x4 in = p.x[idx];
-    u32x4 out;
-    float s = 1.0f;
-    u32x4 g = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 ones
-    if (p.rms) {
-      s = p.rms[tok];
-      g = *(const u32x4*)(p.gamma + (tok_head - tok * p.heads) * kHeadDim + 8 * dc);
-    }
+    int row[4];                                     // table row of each pair: axis, position
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      int c = 4 * dc + e;
-      int a = pair_axis(c);
-      int pa = a == 0 ? f + p.f0 : (a == 1 ? h + p.h0 : w + p.w0);
-      float2 cs = tab[(a * kMaxPos + pa) * kTabStride + pair_index(c)];
-      float re = bf16_lo(in[e]) * s * bf16_lo(g[e]), im = bf16_hi(in[e]) * s * bf16_hi(g[e]);
-      out[e] = pack_bf16x2(re * cs.x - im * cs.y, re * cs.y + im * cs.x);
+      const int c = 4 * dc + e;
+      const int a = pair_axis(c);
+      const int pa = a == 0 ? f + p.f0 : (a == 1 ? h + p.h0 : w + p.w0);
+      row[e] = (a * kMaxPos + pa) * kTabStride + pair_index(c);
     }
-    p.y[idx] = out;
+    float2 cs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cs[e] = p.tab[row[e]];
+    const float s = p.rms ? p.rms[tok] : 1.0f;
+    const u32x4* src = p.x + (size_t)tok * p.heads * 16 + dc;
+    u32x4* dst = p.y + (size_t)tok * p.heads * 16 + dc;
+#pragma unroll 4
+    for (int hd = 0; hd < p.heads; ++hd) {
+      const u32x4 in = src[(size_t)hd * 16];
+      if (p.tab_hstride != 0) {
+        const float2* tab = p.tab + hd * p.tab_hstride;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[e] = tab[row[e]];
+      }
+      u32x4 g = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 ones
+      if (p.gamma) g = *(const u32x4*)(p.gamma + (size_t)hd * kHeadDim + 8 * dc);
+      u32x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float re = bf16_lo(in[e]) * s * bf16_lo(g[e]), im = bf16_hi(in[e]) * s * bf16_hi(g[e]);
+        out[e] = pack_bf16x2(re * cs[e].x - im * cs[e].y, re * cs[e].y + im * cs[e].x);
+      }
+      dst[(size_t)hd * 16] = out;
+    }
   }
 }
 

@@ -364,7 +364,7 @@ wanattn_status rope3d_launch(const void* x, void* y, int32_t B, int32_t N, int32
   p.y = (u32x4*)y;
   p.tab = tab;
   p.tab_hstride = hstride;
-  p.chunks = (long long)B * N * heads * 16;
+  p.chunks = (long long)B * N * 16;
   p.N = N;
   p.heads = heads;
   p.H = grid->H;

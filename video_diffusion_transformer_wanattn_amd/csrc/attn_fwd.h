@@ -124,11 +124,6 @@ constexpr int kQueueCounters = 9;  // one per XCD, then the split items
 // against) as kBM float2, index (2 * wave + qb) * 32 + row % 32.
 constexpr int kPartO = kBM * kHeadDim / 4;
 
-// Output staging (epilogue): chunk c of staged row m (0..31 within a 32-row
-// block) sits at chunk position c ^ o_swz(m).  The 8-byte writes are served
-// 32 lanes (rows 0..31 of one half of d) at a time: rows m and m + 16 must
-// not share a chunk position, hence bit 4 of m flips bit 3 of the position.
-__device__ __forceinline__ int o_swz(int m) { return (m & 15) ^ ((m >> 1) & 8); }
 // K row slot of physical key t inside a tile: swap bits 2 and 3 (an involution)
 __device__ __forceinline__ int k_slot(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 // 16-byte chunk swizzles (chunk index 0..15 within a 256-byte row)
@@ -899,7 +894,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
     }
     for (; t < nt; ++t) tile_step(t, t + 1, t + 3, Mask{}, t);
 
-    // 32 staged output rows (row m's chunk c at c ^ o_swz(m), 256 bytes a row)
+    // 32 staged output rows (row m's chunk c at c ^ (m & 15), 256 bytes a row)
     // to O: lane (sr, sc) = (lane / 16, lane % 16) writes chunk sc of rows
     // 4 it + sr, 1 KiB (4 whole rows) per instruction.  All reads are issued
     // before the stores; a block that reaches past the last token checks each
@@ -910,7 +905,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
   #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int row = 4 * it + sr;
-        w[it] = *(const u32x4*)(rows + row * kRowBytes + 16 * (sc ^ o_swz(row)));
+        w[it] = *(const u32x4*)(rows + row * kRowBytes + 16 * (sc ^ (row & 15)));
       }
       const size_t step = 4 * ((size_t)p.heads * kHeadDim);
       if (whole) {
@@ -999,7 +994,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
             u32x2 w;
             w[0] = pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv);
             w[1] = pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv);
-            *(u32x2*)(orows + r * kRowBytes + 16 * ((4 * db + g4) ^ o_swz(r)) + 8 * hh) = w;
+            *(u32x2*)(orows + r * kRowBytes + 16 * ((4 * db + g4) ^ (r & 15)) + 8 * hh) = w;
           }
         const int irow0 = i0 + wave * 64 + qb * 32 + sr;
         store_rows(orows, p.o + ((size_t)b * p.N + irow0) * row_stride + (size_t)head * kHeadDim + 8 * sc,
@@ -1019,7 +1014,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnParams p_arg)
           u32x2 w;
           w[0] = pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv);
           w[1] = pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv);
-          *(u32x2*)(orows + row * kRowBytes + 16 * ((4 * db + g4) ^ o_swz(r)) + 8 * hh) = w;
+          *(u32x2*)(orows + row * kRowBytes + 16 * ((4 * db + g4) ^ (row & 15)) + 8 * hh) = w;
         }
     }
     const int sr = lane >> 4, sc = lane & 15;

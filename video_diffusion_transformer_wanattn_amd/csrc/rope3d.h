@@ -5,13 +5,15 @@
 // and width segments of the head (44/42/42 wide) and multiplies q or k by them
 // as complex numbers.
 //
-// Memory-bound: a thread takes one 16-byte chunk (4 complex pairs) of one
-// token and rotates it in every head: the token's (f, h, w) and the chunk's
-// four (cos, sin) pairs are found once (with per-head tables, per head) and
-// the heads' chunks are then loaded, rotated and stored.  16 consecutive
-// threads cover one 256-byte head vector of a token, so every load and store
-// instruction moves whole 256-byte runs.  Bytes moved per element: 2 read + 2
-// written.
+// Memory-bound: one wave per token row (heads x 256 bytes, contiguous): lane
+// (hq, dc) = (lane / 16, lane % 16) takes 16-byte chunk dc (4 complex pairs)
+// of heads hq, hq + 4, hq + 8, ..., so every load and store instruction moves
+// 1 KiB of the row (4 whole head vectors).  The token's (f, h, w) and the
+// chunk's four (cos, sin) pairs are found once per wave and lane (with
+// per-head tables, per head).  Measured at 75,600 tokens x 40 heads: 5.3 TB/s,
+// against 4.9 TB/s for waves over 4 tokens' rows (256 bytes of each per
+// instruction) and 4.0 TB/s with 8 loads per lane issued before any rotation.
+// Bytes moved per element: 2 read + 2 written.
 #pragma once
 
 #include "common.h"
@@ -27,17 +29,18 @@ struct RopeParams {
   // row] * gamma[head * 128 + d], rms indexed by b * N + n
   const float* rms;
   const uint16_t* gamma;
-  long long chunks;  // B * N * 16: (token, 16-byte chunk) pairs
+  long long tokens;  // B * N
   int N, heads, H, W;
   int f0, h0, w0;
   double inv_hw, inv_w;
 };
 
 __global__ void __launch_bounds__(256) rope3d_kernel(RopeParams p) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < p.chunks; idx += stride) {
-    const int dc = (int)(idx & 15);                 // 16-byte chunk in the head vector
-    const unsigned tok = (unsigned)(idx >> 4);      // b * N + n (fewer than 2^31 tokens fit in memory)
+  const int lane = threadIdx.x & 63;
+  const int hq = lane >> 4, dc = lane & 15;
+  const long long waves = (long long)gridDim.x * (blockDim.x >> 6);
+  for (long long t = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < p.tokens; t += waves) {
+    const unsigned tok = (unsigned)t;               // b * N + n (fewer than 2^31 tokens fit in memory)
     const int n = (int)(tok % (unsigned)p.N);       // token index in its batch
     int f, rem, h, w;
     divmod(n, p.H * p.W, p.inv_hw, f, rem);
@@ -57,7 +60,7 @@ __global__ void __launch_bounds__(256) rope3d_kernel(RopeParams p) {
     const u32x4* src = p.x + (size_t)tok * p.heads * 16 + dc;
     u32x4* dst = p.y + (size_t)tok * p.heads * 16 + dc;
 #pragma unroll 4
-    for (int hd = 0; hd < p.heads; ++hd) {
+    for (int hd = hq; hd < p.heads; hd += 4) {
       const u32x4 in = src[(size_t)hd * 16];
       if (p.tab_hstride != 0) {
         const float2* tab = p.tab + hd * p.tab_hstride;

@@ -364,7 +364,7 @@ wanattn_status rope3d_launch(const void* x, void* y, int32_t B, int32_t N, int32
   p.y = (u32x4*)y;
   p.tab = tab;
   p.tab_hstride = hstride;
-  p.chunks = (long long)B * N * 16;
+  p.tokens = (long long)B * N;
   p.N = N;
   p.heads = heads;
   p.H = grid->H;
@@ -374,8 +374,10 @@ wanattn_status rope3d_launch(const void* x, void* y, int32_t B, int32_t N, int32
   p.w0 = grid->w0;
   p.inv_hw = 1.0 / ((double)grid->H * grid->W);
   p.inv_w = 1.0 / (double)grid->W;
-  long long blocks = (p.chunks + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
+  // one wave per token, 4 per workgroup; the grid-stride loop only matters
+  // past 2^24 workgroups
+  long long blocks = (p.tokens + 3) / 4;
+  if (blocks > (1LL << 24)) blocks = 1LL << 24;
   hipLaunchKernelGGL(rope3d_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return launched("rope3d");
 }

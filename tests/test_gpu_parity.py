@@ -189,9 +189,12 @@ def test_deterministic():
     np.testing.assert_array_equal(a, b)
 
 
-def test_rope3d_matches_oracle():
+@pytest.mark.parametrize("heads", [3, 1, 5, 9])
+def test_rope3d_matches_oracle(heads):
+    # one wave per token row, lane group hq taking heads hq, hq + 4, ...:
+    # head counts below 4 and not a multiple of 4 leave groups idle or uneven
     grid = (5, 7, 9)
-    x = gen((2, 315, 3, 128), 800, 1, 1.0)
+    x = gen((2, 315, heads, 128), 800 + heads, 1, 1.0)
     ref = oracle.rope3d(x, grid, THETA, offsets=(4, 2, 1))
     xd = to_dev(x)
     y = from_dev(wa.rope3d(xd, grid, THETA, offsets=(4, 2, 1)))
